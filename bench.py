@@ -1,0 +1,320 @@
+#!/usr/bin/env python3
+"""Benchmark one step of the paged-KV hot path on one MI355X.
+
+A step is one pass of the whole hot path over one batch: the slot-mapped KV
+write of the step's new tokens, then attention for every layer of the
+workload (split-K decode + reduce, or the chunked-prefill kernel). Inputs are
+seeded synthetic data (``synth``) already resident in HBM when timing starts.
+
+Default workload: the Qwen3-0.6B-shaped decode step (B=4, Hq=16, Hkv=8,
+D=128, bf16, 2048-token contexts with a 512-token shared prefix chain, a
+2048 MiB pool). Its 26 MiB of live K/V would fit the GPU's last-level cache, so
+the pool holds several independent batches ("waves", each with its own
+prefix chain) and consecutive steps serve different ones; a step still
+processes exactly one batch.
+
+Prints one JSON line: the step throughput (``value``), a roofline entry for
+the dominant kernel (its average launch time from HIP events recorded by the
+library on the launch stream over the timed region) and the CPU oracle's rate
+on a bounded sample of the same workload.
+
+    python bench.py [--workload qwen3|mixed|hybrid|prefill|tiny] [--steps K] [--warmup W]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "paged decode attn: KV GB/s & % HBM peak; prefill-chunk TFLOP/s & % MFMA"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+DEFAULT_WAVES = {"qwen3": 16}
+DEFAULT_STEPS = {"qwen3": 400, "mixed": 100, "hybrid": 100, "prefill": 20, "tiny": 200}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def decode_bytes(wl, tabs, rows):
+    """Algorithmic bytes of one decode step over ``rows`` (every layer):
+    distinct live K/V token rows (shared prefix blocks once) + Q + O + the
+    block-table entries the rows attend through."""
+    esz = 2 if wl.dtype == "bf16" else 4
+    total = 0
+    for L in wl.layers:
+        src = L.alias_of or L.name
+        t = tabs[src]["tables"]
+        seen = set()
+        nblk = 0
+        for b in rows:
+            n = int(wl.seq_lens[b])
+            lo = max(0, n - L.window) if L.window else 0
+            for p in range(lo, n):
+                seen.add((int(t[b][p // wl.block_size]), p % wl.block_size))
+            nblk += -(-n // wl.block_size) - lo // wl.block_size
+        kv = len(seen) * wl.hkv * wl.head_dim * esz * 2
+        qo = 2 * len(rows) * wl.hq * wl.head_dim * esz
+        total += kv + qo + 4 * nblk
+    return total
+
+
+def decode_kv_bytes_per_layer(wl, tabs, rows):
+    out = {}
+    for L in wl.layers:
+        out[L.name] = decode_bytes(_only(wl, L), tabs, rows)
+    return out
+
+
+def _only(wl, L):
+    import copy
+
+    w = copy.copy(wl)
+    w.layers = [L]
+    return w
+
+
+def prefill_flops(wl, rows=None):
+    """4 * D per (query head, visible key) pair: Q.K and P.V, multiply-adds x2."""
+    pairs = 0
+    cu = np.concatenate([[0], np.cumsum(wl.chunk_lens)])
+    for b in range(wl.batch):
+        C = int(wl.chunk_lens[b])
+        P = int(wl.seq_lens[b]) - C
+        W = wl.layers[0].window
+        for i in range(C):
+            if rows is not None and int(cu[b]) + i not in rows:
+                continue
+            a = P + i
+            lo = max(0, a - W + 1) if W else 0
+            pairs += a + 1 - lo
+    return 4.0 * wl.head_dim * wl.hq * pairs
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+
+        return max([int(x.get("num_threads", 1)) for x in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        return 1
+
+
+def cpu_baseline(wl, args):
+    """Time the float64 oracle on a bounded sample of the same workload."""
+    import oracle  # noqa: F401  (imported only on this leg)
+    import runner
+    from oracle import RefAllocator
+    import synth
+
+    tabs = synth.build_tables(RefAllocator, wl)
+    pools = runner.oracle_setup(wl, tabs)
+    budget = args.cpu_seconds
+    if wl.kind == "decode":
+        rows = list(range(wl.wave_size or wl.batch))
+        sub = _subset(wl, rows)
+        sub_pools = pools
+        work = decode_bytes(wl, tabs, rows)
+        unit, scale = "GB/s", 1e9
+        sample = f"oracle decode of {len(rows)} rows (every layer), repeated"
+        fn = lambda: runner.oracle_step(sub, sub_pools)  # noqa: E731
+    else:
+        T = int(wl.chunk_lens.sum())
+        rows = sorted(set(np.linspace(0, T - 1, 128).astype(int).tolist()))
+        work = prefill_flops(wl, set(rows))
+        unit, scale = "TFLOP/s", 1e12
+        sample = f"oracle prefill of {len(rows)} query rows spread over the chunk, all heads, repeated"
+        fn = lambda: runner.oracle_step(wl, pools, rows=rows)  # noqa: E731
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget or reps >= 1000:
+            break
+    rate = work * reps / el / scale
+    return {"value": rate, "unit": unit, "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{sample} {reps}x in {el:.1f} s on {len(os.sched_getaffinity(0))} host cores "
+                      f"(BLAS threads {blas_threads()})"}
+
+
+def _subset(wl, rows):
+    import copy
+
+    sub = copy.copy(wl)
+    sub.batch = len(rows)
+    sub.seq_lens = wl.seq_lens[rows]
+    sub.tokens = [wl.tokens[r] for r in rows]
+    sub.layers = []
+    for L in wl.layers:
+        L2 = copy.copy(L)
+        L2.q = L.q[rows]
+        sub.layers.append(L2)
+    return sub
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="qwen3", choices=["qwen3", "mixed", "hybrid", "prefill", "tiny"])
+    ap.add_argument("--waves", type=int, default=None, help="independent batches rotated through")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only; a multi-GPU run is not available "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import block_paged_kv_amd as pk
+    import runner
+    import synth
+
+    steps = args.steps or DEFAULT_STEPS[args.workload]
+    waves = args.waves or DEFAULT_WAVES.get(args.workload, 1)
+    kw = {"waves": waves} if args.workload == "qwen3" else {}
+    log(f"[bench] building workload {args.workload} ({kw})")
+    wl = synth.make(args.workload, **kw)
+    R = waves if args.workload == "qwen3" else 1
+    wsz = wl.wave_size or wl.batch
+    tabs = synth.build_tables(pk.Allocator, wl)
+    log("[bench] writing cached context to device pools")
+    dev = runner.gpu_setup(wl, tabs, fill=0.0)
+    torch.cuda.synchronize()
+
+    # Prepared calls for every step variant (one per wave).
+    calls = []
+    if wl.kind == "decode":
+        outs = {L.name: torch.empty((wsz,) + tuple(dev[L.name]["q"].shape[1:]), dtype=dev[L.name]["q"].dtype,
+                                    device="cuda") for L in wl.layers}
+    else:
+        outs = {L.name: torch.empty_like(dev[L.name]["q"]) for L in wl.layers}
+    ws = runner.gpu_workspace(_subset(wl, list(range(wsz))) if R > 1 else wl, dev)
+    for r in range(R):
+        rows = slice(r * wsz, (r + 1) * wsz)
+        seq = []
+        for L in wl.layers:
+            if L.alias_of:
+                continue
+            d = dev[L.name]
+            nt = wl.new_tokens
+            t0 = sum(nt[:r * wsz])
+            t1 = sum(nt[:(r + 1) * wsz])
+            seq.append(pk.paged_kv_write(d["k_pool"], d["v_pool"], d["step_k"][t0:t1], d["step_v"][t0:t1],
+                                         d["step_slots"][t0:t1], prepare=True))
+        for L in wl.layers:
+            d = dev[L.name]
+            if wl.kind == "decode":
+                seq.append(pk.paged_attn_decode(
+                    outs[L.name], d["q"][rows], d["k_pool"], d["v_pool"], d["tables"][rows],
+                    dev["_seq_lens"][rows], wl.scale, int(wl.seq_lens[rows].max()),
+                    sliding_window=L.window, partition_tokens=wl.partition_tokens, workspace=ws,
+                    prepare=True))
+            else:
+                seq.append(pk.paged_attn_prefill_chunk(
+                    outs[L.name], d["q"], d["k_pool"], d["v_pool"], d["tables"], dev["_cu_q"],
+                    dev["_seq_lens"], int(wl.chunk_lens.max()), wl.scale, sliding_window=L.window,
+                    prepare=True))
+        calls.append(seq)
+
+    def step(i):
+        for c in calls[i % R]:
+            c()
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    pk.trace_reset()
+    pk.trace_enable(True)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {steps} steps")
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    pk.trace_enable(False)
+    ms_per_step = (t1 - t0) * 1e3 / steps
+
+    if wl.kind == "decode":
+        per_wave = [decode_bytes(wl, tabs, list(range(r * wsz, (r + 1) * wsz))) for r in range(R)]
+        work = float(np.mean([per_wave[(args.warmup + i) % R] for i in range(steps)]))
+        value = work / (ms_per_step * 1e-3) / 1e9
+        unit = "GB/s"
+        kern = "decode_partial"
+        k_ms, k_n = pk.trace_query(kern)
+        achieved = work * steps / (k_ms * 1e-3) / 1e9  # all partial launches of the region
+        peak, bound, runit = HBM_PEAK_GBS, "hbm", "GB/s"
+    else:
+        work = prefill_flops(wl)
+        value = work / (ms_per_step * 1e-3) / 1e12
+        unit = "TFLOP/s"
+        kern = "prefill"
+        k_ms, k_n = pk.trace_query(kern)
+        achieved = work * steps / (k_ms * 1e-3) / 1e12
+        peak, bound, runit = MFMA_BF16_PEAK_TFLOPS, "mfma", "TFLOP/s"
+    kernels = {}
+    for name in pk.KERNELS:
+        ms, n = pk.trace_query(name)
+        if n:
+            kernels[name] = {"launches": n, "avg_us": round(ms * 1e3 / n, 3)}
+    log(f"[bench] kernels: {kernels}")
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": {"qwen3": "qwen3-0.6b-shaped decode step", "mixed": "mixed-length continuous-batching decode",
+                         "hybrid": "gemma-style hybrid sliding/full/kv-shared decode",
+                         "prefill": "chunked prefill over cached prefix", "tiny": "tiny fp32 decode"}[args.workload],
+            "batch": int(wsz), "num_q_heads": wl.hq, "num_kv_heads": wl.hkv, "head_dim": wl.head_dim,
+            "block_size": wl.block_size, "max_seq_len": wl.max_seq_len,
+            "layers": [L.name for L in wl.layers], "waves_rotated": R,
+            "pool_blocks": [L.num_blocks for L in wl.layers if not L.alias_of],
+        },
+        "roofline": {
+            "kernel": kern,
+            "bound": bound,
+            "achieved": round(achieved, 3),
+            "peak": peak,
+            "unit": runit,
+            "frac": round(achieved / peak, 4),
+            "traffic": None,
+            "avg_launch_us": round(k_ms * 1e3 / max(k_n, 1), 3),
+            "launches": k_n,
+            "work_per_step": work,
+        },
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(wl, args)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

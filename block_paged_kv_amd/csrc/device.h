@@ -1,0 +1,61 @@
+// Device-side helpers shared by the gfx950 kernels of libpagedkv.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pagedkv.h"
+
+namespace pagedkv {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+// bf16 is carried as raw 16-bit patterns; a 32-bit word holds two of them,
+// the lower-addressed element in the low half.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// Two bf16 products summed into a float accumulator (v_dot2_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Lane permutation inside a 16-lane DPP row.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+
+// Sum over aligned groups of R lanes (R in {1,2,4,8,16}); every lane of a
+// group receives the group total. quad_perm [1,0,3,2], quad_perm [2,3,0,1],
+// row_half_mirror and row_mirror pair each lane with a partner in the
+// other half of its current group.
+template <int R>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (R >= 2) x += dpp_mov<0xB1>(x);
+  if constexpr (R >= 4) x += dpp_mov<0x4E>(x);
+  if constexpr (R >= 8) x += dpp_mov<0x141>(x);
+  if constexpr (R >= 16) x += dpp_mov<0x140>(x);
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+}  // namespace pagedkv

@@ -1,0 +1,359 @@
+// Chunked-prefill attention over a block-paged cache, bf16 MFMA (gfx950).
+//
+// What is computed (mlx-node perf doc, paged-attention knobs table: prefill
+// chunk size and the bridge that reads prefill K/V through the pages): every
+// query of a chunk at absolute position a = P + i attends, with plain softmax,
+// to the keys [lo, a] of its request, K/V read in place through the request's
+// block table; the chunk's own K/V was written first.
+//
+// How (ours):
+//   * Query rows are (position, query head) pairs of one KV head, packed
+//     position-major, so the G query heads sharing a KV head share every K/V
+//     tile. A workgroup of 4 waves owns 128 rows; each wave owns 32.
+//   * K/V tiles of 64 keys (whole blocks) are staged in LDS: K row-major
+//     (key, head_dim), V transposed (head_dim, key) by a 4x8 register
+//     transpose so the P.V operand reads consecutive keys.
+//   * S^T = K Q^T and O += P V run on v_mfma_f32_16x16x32_bf16 with fp32
+//     accumulators; the S^T accumulator layout (one query per lane, 4 keys per
+//     register group) is exactly the A-operand layout P needs, once converted
+//     to bf16, so no shuffle sits between the two products.
+//   * Online softmax in fp32 (log2 units); the causal / window mask is applied
+//     only on tiles that straddle a row's range.
+//   * The 1-D grid is remapped so consecutive tiles of one KV head land on one
+//     XCD (round-robin dispatch puts workgroup i on XCD i % 8): that XCD's L2
+//     then serves the head's K/V to all of its tiles.
+
+#include <cmath>
+
+#include "device.h"
+#include "runtime.h"
+
+namespace pagedkv {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kRowsPerWave = 32;
+constexpr int kTileM = kWaves * kRowsPerWave;  // 128 query rows per workgroup
+constexpr int kTileN = 64;                      // keys per K/V tile
+constexpr int kNumXcd = 8;
+
+typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+
+struct PrefillParams {
+  uint16_t* out;
+  const uint16_t* q;
+  const uint16_t* k_pool;
+  const uint16_t* v_pool;
+  const int32_t* bt;
+  const int32_t* cu_q;
+  const int32_t* seq_lens;
+  int32_t mb, hq, hkv, group, bs_log2, nb, window;
+  int32_t tiles_per_head;   // ceil(max_q_len * group / kTileM)
+  int32_t work_items;       // batch * hkv * tiles_per_head
+  int32_t per_xcd;          // ceil(work_items / kNumXcd)
+  float scale_log2;
+};
+
+__device__ __forceinline__ floatx4_t mfma16x16x32(const uint4& a, const uint4& b, floatx4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v, a),
+                                                 __builtin_bit_cast(bf16x8v, b), c, 0, 0, 0);
+}
+
+template <int D>
+__global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillParams a) {
+  constexpr int KSTR = D + 8;        // K row stride in LDS (elements): spreads banks
+  constexpr int VSTR = kTileN + 8;   // V^T row stride in LDS (elements)
+  constexpr int DCH = D / 8;         // 16-byte chunks per key row
+  constexpr int KS = D / 32;         // MFMA k-steps over head_dim
+  constexpr int NT = D / 16;         // output column tiles
+  constexpr float kNegInf = -INFINITY;
+
+  __shared__ __attribute__((aligned(16))) uint16_t k_s[kTileN * KSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t vt_s[D * VSTR];
+
+  // XCD-aware work mapping: XCD x takes work items [x*per_xcd, (x+1)*per_xcd).
+  const int lin = blockIdx.x;
+  const int item = (lin % kNumXcd) * a.per_xcd + lin / kNumXcd;
+  if (item >= a.work_items) return;
+  const int tile = item % a.tiles_per_head;
+  const int kvh = (item / a.tiles_per_head) % a.hkv;
+  const int b = item / (a.tiles_per_head * a.hkv);
+
+  const int q0 = a.cu_q[b];
+  const int C = a.cu_q[b + 1] - q0;
+  const int n = a.seq_lens[b];
+  const int P = n - C;
+  const int G = a.group;
+  const int rows = C * G;
+  const int r_first = tile * kTileM;
+  if (r_first >= rows || P < 0) return;
+  const int r_last = min(r_first + kTileM, rows) - 1;
+  const int a_min = P + r_first / G;
+  const int a_max = P + r_last / G;
+  const int lo_min = a.window > 0 ? max(0, a_min - a.window + 1) : 0;
+  const int lo_max = a.window > 0 ? max(0, a_max - a.window + 1) : 0;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int lq = lane & 15;   // query column inside a 16-wide tile
+  const int lg = lane >> 4;   // lane group 0..3
+
+  // Query rows of this lane in the S^T layout: wave rows 16j + lq.
+  int qpos[2], qlo[2];
+  bool qvalid[2];
+  uint4 qreg[2][KS];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = r_first + wave * kRowsPerWave + 16 * j + lq;
+    qvalid[j] = r <= r_last;
+    const int pos = qvalid[j] ? r / G : 0;
+    const int g = qvalid[j] ? r - pos * G : 0;
+    qpos[j] = P + pos;
+    qlo[j] = a.window > 0 ? max(0, qpos[j] - a.window + 1) : 0;
+    const uint16_t* qrow = a.q + (static_cast<size_t>(q0 + pos) * a.hq + kvh * G + g) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qreg[j][ks] = qvalid[j] ? *reinterpret_cast<const uint4*>(qrow + ks * 32 + lg * 8)
+                              : make_uint4(0, 0, 0, 0);
+  }
+
+  floatx4_t o[2][NT];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) o[j][nt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  float m[2] = {kNegInf, kNegInf};
+  float l[2] = {0.f, 0.f};
+
+  const int32_t* bt = a.bt + static_cast<size_t>(b) * a.mb;
+  const int bs_mask = (1 << a.bs_log2) - 1;
+  const int kt_begin = lo_min / kTileN;
+  const int kt_end = a_max / kTileN;  // inclusive
+
+  for (int kt = kt_begin; kt <= kt_end; ++kt) {
+    const int ts = kt * kTileN;
+    __syncthreads();  // previous tile fully consumed
+    // ---- stage K (row-major) -------------------------------------------------
+    for (int c = tid; c < kTileN * DCH; c += kWaves * 64) {
+      const int key = c / DCH;
+      const int dc = c - key * DCH;
+      const int kp = ts + key;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (kp < n) {
+        const int lb = kp >> a.bs_log2;
+        const int phys = lb < a.mb ? bt[lb] : 0;
+        if (phys > 0 && phys < a.nb) {
+          const size_t row = ((static_cast<size_t>(phys) * a.hkv + kvh) << a.bs_log2) + (kp & bs_mask);
+          v = *reinterpret_cast<const uint4*>(a.k_pool + row * D + dc * 8);
+        }
+      }
+      *reinterpret_cast<uint4*>(&k_s[key * KSTR + dc * 8]) = v;
+    }
+    // ---- stage V transposed: unit = 4 keys x 8 head_dim elements -------------
+    for (int u = tid; u < (kTileN / 4) * DCH; u += kWaves * 64) {
+      const int kg = u % (kTileN / 4);
+      const int dc = u / (kTileN / 4);
+      uint4 w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kp = ts + kg * 4 + i;
+        w[i] = make_uint4(0, 0, 0, 0);
+        if (kp < n) {
+          const int lb = kp >> a.bs_log2;
+          const int phys = lb < a.mb ? bt[lb] : 0;
+          if (phys > 0 && phys < a.nb) {
+            const size_t row = ((static_cast<size_t>(phys) * a.hkv + kvh) << a.bs_log2) + (kp & bs_mask);
+            w[i] = *reinterpret_cast<const uint4*>(a.v_pool + row * D + dc * 8);
+          }
+        }
+      }
+      const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&w[0]);
+      const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&w[1]);
+      const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&w[2]);
+      const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&w[3]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // head_dim element 2e: low halves; 2e+1: high halves (keys 0..3 in order)
+        uint2 lo2, hi2;
+        lo2.x = __builtin_amdgcn_perm(w1[e], w0[e], 0x05040100u);
+        lo2.y = __builtin_amdgcn_perm(w3[e], w2[e], 0x05040100u);
+        hi2.x = __builtin_amdgcn_perm(w1[e], w0[e], 0x07060302u);
+        hi2.y = __builtin_amdgcn_perm(w3[e], w2[e], 0x07060302u);
+        *reinterpret_cast<uint2*>(&vt_s[(dc * 8 + 2 * e) * VSTR + kg * 4]) = lo2;
+        *reinterpret_cast<uint2*>(&vt_s[(dc * 8 + 2 * e + 1) * VSTR + kg * 4]) = hi2;
+      }
+    }
+    __syncthreads();
+
+    // ---- S^T = K Q^T : 4 key sub-tiles x 2 query tiles ----------------------
+    floatx4_t s[2][4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4) s[j][t4] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint4 ka = *reinterpret_cast<const uint4*>(&k_s[(t4 * 16 + lq) * KSTR + ks * 32 + lg * 8]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) s[j][t4] = mfma16x16x32(ka, qreg[j][ks], s[j][t4]);
+      }
+
+    // ---- online softmax (lane: query 16j+lq, keys ts + 16*t4 + 4*lg + i) ------
+    const bool need_mask = (ts + kTileN - 1 > a_min) || (ts < lo_max);
+    uint4 pa[2][2];  // P as bf16 A operands: [query tile][32-key step]
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v = s[j][t4][i] * a.scale_log2;
+          if (need_mask) {
+            const int kp = ts + t4 * 16 + lg * 4 + i;
+            if (!(kp >= qlo[j] && kp <= qpos[j] && qvalid[j])) v = kNegInf;
+          }
+          s[j][t4][i] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(m[j], mx);
+      const float mref = mnew == kNegInf ? 0.f : mnew;
+      const float alpha = fast_exp2(m[j] - mref);
+      m[j] = mnew;
+      float ls = 0.f;
+      float pr[4][4];
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pr[t4][i] = fast_exp2(s[j][t4][i] - mref);
+          ls += pr[t4][i];
+        }
+      l[j] = l[j] * alpha + ls;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        pa[j][kk].x = pack_bf16x2(pr[2 * kk][0], pr[2 * kk][1]);
+        pa[j][kk].y = pack_bf16x2(pr[2 * kk][2], pr[2 * kk][3]);
+        pa[j][kk].z = pack_bf16x2(pr[2 * kk + 1][0], pr[2 * kk + 1][1]);
+        pa[j][kk].w = pack_bf16x2(pr[2 * kk + 1][2], pr[2 * kk + 1][3]);
+      }
+      // Rescale O rows (O layout: lane holds queries 16j + 4*lg + i).
+      if (!__all(alpha == 1.f)) {
+        float al[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * lg + i);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[j][nt][i] *= al[i];
+      }
+    }
+
+    // ---- O += P V -------------------------------------------------------------
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const uint16_t* vrow = &vt_s[(nt * 16 + lq) * VSTR + kk * 32 + lg * 4];
+        const uint2 v0 = *reinterpret_cast<const uint2*>(vrow);
+        const uint2 v1 = *reinterpret_cast<const uint2*>(vrow + 16);
+        const uint4 vb = make_uint4(v0.x, v0.y, v1.x, v1.y);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) o[j][nt] = mfma16x16x32(pa[j][kk], vb, o[j][nt]);
+      }
+  }
+
+  // ---- normalise and store --------------------------------------------------
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    float lt = l[j];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    float inv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float li = __shfl(lt, 4 * lg + i);
+      inv[i] = li > 0.f ? 1.f / li : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = r_first + wave * kRowsPerWave + 16 * j + 4 * lg + i;
+      if (r > r_last) continue;
+      const int pos = r / G;
+      const int g = r - pos * G;
+      uint16_t* orow = a.out + (static_cast<size_t>(q0 + pos) * a.hq + kvh * G + g) * D;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        orow[nt * 16 + lq] = static_cast<uint16_t>(f32_to_bf16_bits(o[j][nt][i] * inv[i]));
+    }
+  }
+}
+
+}  // namespace
+}  // namespace pagedkv
+
+using namespace pagedkv;
+
+extern "C" int32_t paged_attn_prefill_chunk(void* out, const void* q, const void* k_pool,
+                                            const void* v_pool, const int32_t* block_tables,
+                                            int32_t max_blocks_per_seq, const int32_t* cu_q_lens,
+                                            const int32_t* seq_lens, int32_t batch,
+                                            int32_t total_q, int32_t max_q_len,
+                                            int32_t num_q_heads, int32_t num_kv_heads,
+                                            int32_t head_dim, int32_t block_size,
+                                            int32_t num_blocks, float scale,
+                                            int32_t sliding_window, int32_t dtype, void* stream) {
+  if (dtype != PAGED_BF16) return fail(PAGED_ERR_DTYPE, "prefill supports bf16 only");
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256)
+    return fail(PAGED_ERR_INVALID_ARG, "head_dim must be 64, 128 or 256 (got %d)", head_dim);
+  if (!pow2_in(block_size, 8, 64))
+    return fail(PAGED_ERR_INVALID_ARG, "block_size must be a power of two in [8, 64]");
+  if (num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads)
+    return fail(PAGED_ERR_INVALID_ARG, "need num_q_heads a positive multiple of num_kv_heads");
+  if (batch < 0 || total_q < 0 || max_q_len < 0 || max_blocks_per_seq < 1 || num_blocks < 1 ||
+      sliding_window < 0)
+    return fail(PAGED_ERR_INVALID_ARG, "bad size argument");
+  if (!std::isfinite(scale)) return fail(PAGED_ERR_INVALID_ARG, "scale must be finite");
+  if (batch == 0 || total_q == 0 || max_q_len == 0) return ok();
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !cu_q_lens || !seq_lens)
+    return fail(PAGED_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
+    return fail(PAGED_ERR_INVALID_ARG, "misaligned pointer");
+  const int group = num_q_heads / num_kv_heads;
+  const int64_t tiles = (static_cast<int64_t>(max_q_len) * group + kTileM - 1) / kTileM;
+  const int64_t items = tiles * num_kv_heads * batch;
+  if (items > (1LL << 30)) return fail(PAGED_ERR_INVALID_ARG, "problem too large");
+  PrefillParams prm{};
+  prm.out = static_cast<uint16_t*>(out);
+  prm.q = static_cast<const uint16_t*>(q);
+  prm.k_pool = static_cast<const uint16_t*>(k_pool);
+  prm.v_pool = static_cast<const uint16_t*>(v_pool);
+  prm.bt = block_tables;
+  prm.cu_q = cu_q_lens;
+  prm.seq_lens = seq_lens;
+  prm.mb = max_blocks_per_seq;
+  prm.hq = num_q_heads;
+  prm.hkv = num_kv_heads;
+  prm.group = group;
+  prm.bs_log2 = ilog2(block_size);
+  prm.nb = num_blocks;
+  prm.window = sliding_window;
+  prm.tiles_per_head = static_cast<int32_t>(tiles);
+  prm.work_items = static_cast<int32_t>(items);
+  prm.per_xcd = static_cast<int32_t>((items + kNumXcd - 1) / kNumXcd);
+  prm.scale_log2 = scale * 1.4426950408889634f;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid(static_cast<unsigned>(prm.per_xcd * kNumXcd));
+  const dim3 block(kWaves * 64);
+  LaunchTrace tr(PAGED_KERNEL_PREFILL, s);
+  if (head_dim == 64) prefill_kernel<64><<<grid, block, 0, s>>>(prm);
+  else if (head_dim == 128) prefill_kernel<128><<<grid, block, 0, s>>>(prm);
+  else prefill_kernel<256><<<grid, block, 0, s>>>(prm);
+  tr.finish();
+  return check_launch("paged_attn_prefill_chunk");
+}

@@ -1,0 +1,44 @@
+// Host-side runtime shared by the launchers: device facts, launch timing and
+// argument checks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pagedkv.h"
+#include "status.h"
+
+namespace pagedkv {
+
+// Compute units of the current device (cached per device); 0 on failure.
+int device_cu_count();
+
+// Records HIP events around one launch when tracing is on.
+class LaunchTrace {
+ public:
+  LaunchTrace(int kernel, hipStream_t stream);
+  void finish();  // record the end event (call right after the launch)
+ private:
+  int kernel_;
+  hipStream_t stream_;
+  hipEvent_t start_ = nullptr;
+};
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline int esize_of(int32_t dtype) { return dtype == PAGED_BF16 ? 2 : dtype == PAGED_F32 ? 4 : 0; }
+
+inline bool pow2_in(int32_t x, int32_t lo, int32_t hi) {
+  return x >= lo && x <= hi && (x & (x - 1)) == 0;
+}
+
+inline int ilog2(int32_t x) {
+  int r = 0;
+  while ((1 << r) < x) ++r;
+  return r;
+}
+
+// Report a launch error (if any) as PAGED_ERR_HIP.
+int32_t check_launch(const char* what);
+
+}  // namespace pagedkv

@@ -115,6 +115,22 @@ class RefAllocator:
                 self.free.append(b)
 
     # -- lifecycle -------------------------------------------------------
+    def grow(self, new_num_blocks, new_order=None):
+        """Append blocks nb..new_nb-1 to the free tail (the mlx-node paged-cache
+        doc's pool-sizing section grows the pool before evicting)."""
+        new_num_blocks = int(new_num_blocks)
+        if new_num_blocks < self.nb:
+            raise AllocError(ERR_INVALID_ARG, "cannot shrink")
+        added = list(range(self.nb, new_num_blocks)) if new_order is None else [int(x) for x in new_order]
+        if sorted(added) != list(range(self.nb, new_num_blocks)):
+            raise AllocError(ERR_INVALID_ARG, "new_order must be a permutation of the new ids")
+        grow_by = new_num_blocks - self.nb
+        self.ref += [0] * grow_by
+        self.chain_id += [0] * grow_by
+        self.key_of += [None] * grow_by
+        self.free.extend(added)
+        self.nb = new_num_blocks
+
     def add(self, seq_id):
         if int(seq_id) in self.seqs:
             raise AllocError(ERR_STATE, f"sequence {seq_id} exists")

@@ -1,0 +1,189 @@
+"""Run synthetic workloads through the library (GPU side) and the oracle (CPU side).
+
+Two separate halves that share only ``synth``'s inputs:
+
+* ``gpu_*`` -- allocate device pools with torch, write the cached context with
+  ``paged_kv_write`` (untimed set-up), then run one step of the hot path: the
+  step's KV write followed by decode (every layer) or the prefill chunk.
+* ``oracle_*`` -- build float32 pools with ``oracle.kv_write`` from the
+  reference allocator's slot mappings and run ``oracle.decode`` /
+  ``oracle.prefill_chunk`` in float64.
+
+Used by the tests, the smoke check and the benchmark. Nothing here is part of
+the library; the library never imports this module.
+"""
+
+from __future__ import annotations
+
+import os
+import sys
+
+import numpy as np
+
+import synth
+
+VERBOSE = os.environ.get("PAGEDKV_VERBOSE", "0") == "1"
+
+
+def say(msg):
+    if VERBOSE:
+        print(msg, file=sys.stderr, flush=True)
+
+
+# ====================================================================== GPU
+def torch_dtype(wl):
+    import torch
+
+    return torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+
+
+def gpu_setup(wl, tabs, fill=float("nan"), device="cuda"):
+    """Device pools with the cached context written; returns per-layer dicts."""
+    import torch
+
+    import block_paged_kv_amd as pk
+
+    dt = torch_dtype(wl)
+    dev = {}
+    for L in wl.layers:
+        if L.alias_of:
+            continue
+        shape = (L.num_blocks, wl.hkv, wl.block_size, wl.head_dim)
+        kp = torch.full(shape, fill, dtype=dt, device=device)
+        vp = torch.full(shape, fill, dtype=dt, device=device)
+        t = tabs[L.name]
+        sk, sv = synth.setup_kv(wl, L)
+        slots = np.concatenate(t["setup_slots"]) if t["setup_slots"] else np.zeros(0, np.int64)
+        say(f"[gpu] setup write {wl.name}/{L.name}: {slots.shape[0]} tokens")
+        if slots.shape[0]:
+            pk.paged_kv_write(kp, vp, torch.from_numpy(sk).to(device=device, dtype=dt),
+                              torch.from_numpy(sv).to(device=device, dtype=dt),
+                              torch.from_numpy(slots).to(device))
+        stk, stv = synth.step_kv(wl, L)
+        dev[L.name] = dict(
+            k_pool=kp, v_pool=vp,
+            tables=torch.from_numpy(t["tables"]).to(device),
+            step_k=torch.from_numpy(stk).to(device=device, dtype=dt),
+            step_v=torch.from_numpy(stv).to(device=device, dtype=dt),
+            step_slots=torch.from_numpy(np.concatenate(t["step_slots"])).to(device),
+        )
+    for L in wl.layers:
+        if L.alias_of:
+            dev[L.name] = dict(dev[L.alias_of])
+        dev[L.name]["q"] = torch.from_numpy(L.q).to(device=device, dtype=dt)
+        dev[L.name]["window"] = L.window
+    dev["_seq_lens"] = torch.from_numpy(wl.seq_lens.astype(np.int32)).to(device)
+    if wl.kind == "prefill":
+        cu = np.concatenate([[0], np.cumsum(wl.chunk_lens)]).astype(np.int32)
+        dev["_cu_q"] = torch.from_numpy(cu).to(device)
+    return dev
+
+
+def gpu_workspace(wl, dev, partition_tokens=None, max_seq_len=None):
+    """One uint8 workspace large enough for every decode layer of the step."""
+    import torch
+
+    import block_paged_kv_amd as pk
+
+    if wl.kind != "decode":
+        return None
+    part = wl.partition_tokens if partition_tokens is None else partition_tokens
+    msl = wl.max_seq_len if max_seq_len is None else max_seq_len
+    need = max(pk.paged_attn_decode_workspace_bytes(wl.batch, wl.hq, wl.hkv, wl.head_dim,
+                                                    wl.block_size, msl, L.window, part)
+               for L in wl.layers)
+    return torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+
+
+def gpu_step(wl, dev, outs=None, workspace=None, partition_tokens=None, max_seq_len=None,
+             layers=None):
+    """One pass of the hot path: the step's KV writes, then attention per layer."""
+    import torch
+
+    import block_paged_kv_amd as pk
+
+    names = [L.name for L in wl.layers] if layers is None else layers
+    if outs is None:
+        outs = {n: torch.empty_like(dev[n]["q"]) for n in names}
+    for L in wl.layers:
+        if L.alias_of or L.name not in names:
+            continue
+        d = dev[L.name]
+        pk.paged_kv_write(d["k_pool"], d["v_pool"], d["step_k"], d["step_v"], d["step_slots"])
+    part = wl.partition_tokens if partition_tokens is None else partition_tokens
+    msl = wl.max_seq_len if max_seq_len is None else max_seq_len
+    for n in names:
+        d = dev[n]
+        if wl.kind == "decode":
+            pk.paged_attn_decode(outs[n], d["q"], d["k_pool"], d["v_pool"], d["tables"],
+                                 dev["_seq_lens"], wl.scale, msl, sliding_window=d["window"],
+                                 partition_tokens=part, workspace=workspace)
+        else:
+            pk.paged_attn_prefill_chunk(outs[n], d["q"], d["k_pool"], d["v_pool"], d["tables"],
+                                        dev["_cu_q"], dev["_seq_lens"], int(wl.chunk_lens.max()),
+                                        wl.scale, sliding_window=d["window"])
+    return outs
+
+
+# ====================================================================== oracle
+def oracle_setup(wl, tabs_ref):
+    """float32 pools (NaN canaries elsewhere) holding the same tokens as the GPU pools."""
+    import oracle
+
+    pools = {}
+    for L in wl.layers:
+        if L.alias_of:
+            continue
+        shape = (L.num_blocks, wl.hkv, wl.block_size, wl.head_dim)
+        kp = np.full(shape, np.nan, dtype=np.float32)
+        vp = np.full(shape, np.nan, dtype=np.float32)
+        t = tabs_ref[L.name]
+        sk, sv = synth.setup_kv(wl, L)
+        stk, stv = synth.step_kv(wl, L)
+        slots = np.concatenate(t["setup_slots"] + t["step_slots"])
+        kp, vp = oracle.kv_write(kp, vp, np.concatenate([sk, stk]), np.concatenate([sv, stv]), slots,
+                                 wl.block_size)
+        pools[L.name] = (kp, vp, t["tables"])
+    for L in wl.layers:
+        if L.alias_of:
+            pools[L.name] = pools[L.alias_of]
+    return pools
+
+
+def oracle_step(wl, pools, rows=None, layers=None):
+    """float64 reference outputs per layer; ``rows`` limits prefill to some query rows."""
+    import oracle
+
+    out = {}
+    for L in wl.layers:
+        if layers is not None and L.name not in layers:
+            continue
+        kp, vp, tables = pools[L.name]
+        if wl.kind == "decode":
+            out[L.name] = oracle.decode(L.q, kp, vp, tables, wl.seq_lens, wl.scale, L.window,
+                                        wl.block_size)
+        else:
+            cu = np.concatenate([[0], np.cumsum(wl.chunk_lens)]).astype(np.int64)
+            out[L.name] = oracle.prefill_chunk(L.q, kp, vp, tables, cu, wl.seq_lens, wl.scale,
+                                               L.window, wl.block_size, query_rows=rows)
+    return out
+
+
+# ====================================================================== compare
+def compare(gpu, ref, dtype, rows=None):
+    """(max_abs, rel_l2) of a GPU output against the float64 oracle."""
+    g = gpu.double().cpu().numpy()
+    r = np.asarray(ref, dtype=np.float64)
+    if rows is not None:
+        g, r = g[rows], r[rows]
+    err = np.abs(g - r)
+    denom = np.linalg.norm(r)
+    return float(err.max()) if err.size else 0.0, float(np.linalg.norm(g - r) / denom) if denom else 0.0
+
+
+TOL = {"f32": dict(max_abs=1e-5, rel_l2=None), "bf16": dict(max_abs=2e-2, rel_l2=5e-3)}
+
+
+def within(dtype, max_abs, rel_l2):
+    t = TOL[dtype]
+    return max_abs <= t["max_abs"] and (t["rel_l2"] is None or rel_l2 <= t["rel_l2"])

@@ -1,0 +1,106 @@
+"""CPU-only checks of the C ABI: the library loads, exports every declared
+symbol, and rejects bad arguments on the host before touching a device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_paged_kv_amd as pk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedkv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(paged_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 25
+    lib = ctypes.CDLL(pk.LIB_PATH)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    # and the binding declares a signature for each of them
+    assert set(names) <= set(pk._SIGNATURES), set(names) - set(pk._SIGNATURES)
+
+
+def test_abi_version_matches_header():
+    m = re.search(r"#define PAGEDKV_ABI_VERSION (\d+)", open(HEADER).read())
+    assert pk.abi_version() == int(m.group(1))
+
+
+def test_write_argument_errors():
+    L = pk.lib
+    # unknown dtype
+    assert L.paged_kv_write(None, None, None, None, None, 1, 8, 16, 1, 128, 7, None) == pk.PAGED_ERR_DTYPE
+    assert b"dtype" in pk.lib.paged_last_error()
+    # head_dim, block size, nulls
+    assert L.paged_kv_write(None, None, None, None, None, 1, 8, 16, 1, 100, 1, None) == pk.PAGED_ERR_INVALID_ARG
+    assert L.paged_kv_write(None, None, None, None, None, 1, 8, 12, 1, 128, 1, None) == pk.PAGED_ERR_INVALID_ARG
+    assert L.paged_kv_write(None, None, None, None, None, 1, 8, 16, 1, 128, 1, None) == pk.PAGED_ERR_INVALID_ARG
+    # nothing to do is a success without any device call
+    assert L.paged_kv_write(None, None, None, None, None, 0, 8, 16, 1, 128, 1, None) == pk.PAGED_OK
+    # misaligned pointers are rejected
+    assert L.paged_kv_write(16, 16, 16, 17, 8, 1, 8, 16, 1, 128, 1, None) == pk.PAGED_ERR_INVALID_ARG
+
+
+def test_decode_argument_errors():
+    L = pk.lib
+    args = dict(out=None, q=None, k=None, v=None, bt=None, mb=4, sl=None, B=2, hq=6, hkv=4, d=128,
+                bs=16, nb=8, scale=0.1, w=0, part=64, msl=64, ws=None, wsb=0, dt=1, s=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.paged_attn_decode(a["out"], a["q"], a["k"], a["v"], a["bt"], a["mb"], a["sl"], a["B"],
+                                   a["hq"], a["hkv"], a["d"], a["bs"], a["nb"], a["scale"], a["w"],
+                                   a["part"], a["msl"], a["ws"], a["wsb"], a["dt"], a["s"])
+
+    assert call() == pk.PAGED_ERR_INVALID_ARG              # 6 q heads on 4 kv heads
+    assert call(hq=8, part=24) == pk.PAGED_ERR_INVALID_ARG  # partition not a multiple of 16
+    assert call(hq=8, dt=3) == pk.PAGED_ERR_DTYPE
+    assert call(hq=8, scale=float("inf")) == pk.PAGED_ERR_INVALID_ARG
+    assert call(hq=8, B=0) == pk.PAGED_OK                   # empty batch: nothing enqueued
+    assert call(hq=8) == pk.PAGED_ERR_INVALID_ARG           # NULL pointers
+
+
+def test_prefill_argument_errors():
+    L = pk.lib
+    rc = L.paged_attn_prefill_chunk(None, None, None, None, None, 4, None, None, 1, 8, 8, 8, 8, 128,
+                                    16, 8, 0.1, 0, pk.PAGED_F32, None)
+    assert rc == pk.PAGED_ERR_DTYPE
+    rc = L.paged_attn_prefill_chunk(None, None, None, None, None, 4, None, None, 1, 8, 8, 8, 3, 128,
+                                    16, 8, 0.1, 0, pk.PAGED_BF16, None)
+    assert rc == pk.PAGED_ERR_INVALID_ARG
+    rc = L.paged_attn_prefill_chunk(None, None, None, None, None, 4, None, None, 1, 0, 8, 8, 8, 128,
+                                    16, 8, 0.1, 0, pk.PAGED_BF16, None)
+    assert rc == pk.PAGED_OK
+
+
+@pytest.mark.parametrize("B,hq,hkv,d,msl,w,part", [
+    (4, 16, 8, 128, 2048, 0, 128), (32, 32, 8, 128, 8192, 0, 512), (8, 8, 1, 256, 32768, 512, 64),
+    (2, 4, 2, 64, 75, 0, 16), (3, 6, 3, 64, 100, 0, 128)])
+def test_workspace_bytes(B, hq, hkv, d, msl, w, part):
+    span = min(msl, w + 15) if w else msl
+    parts = -(-span // part)
+    expect = 0 if parts == 1 else B * hq * parts * (d + 2) * 4
+    assert pk.paged_attn_decode_workspace_bytes(B, hq, hkv, d, 16, msl, w, part) == expect
+
+
+def test_library_rule_needs_a_device_here():
+    # No GPU in this container: the rule's device query fails cleanly.
+    with pytest.raises(pk.PagedError) as e:
+        pk.paged_attn_decode_partition_tokens(4, 16, 8, 16, 2048, 0)
+    assert e.value.code in (pk.PAGED_ERR_HIP, pk.PAGED_OK) or e.value.code == pk.PAGED_ERR_HIP
+
+
+def test_trace_api_without_launches():
+    pk.trace_reset()
+    assert pk.trace_query("decode_partial") == (0.0, 0)
+    with pytest.raises(KeyError):
+        pk.trace_query("nope")
+    assert pk.lib.paged_trace_query(9, None, None) == pk.PAGED_ERR_INVALID_ARG

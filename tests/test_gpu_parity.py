@@ -1,0 +1,286 @@
+"""GPU parity: the HIP path against the float64 oracle, through the C ABI.
+
+Bit-exact for the KV write, the gather and the block tables; attention within
+max-abs 1e-5 (fp32) or max-abs 2e-2 and relative L2 5e-3 (bf16). Every case
+prints its name before touching the GPU.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+import runner
+import synth
+from oracle import RefAllocator
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pk():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_paged_kv_amd
+
+    return block_paged_kv_amd
+
+
+def announce(msg):
+    print(f"\n[case] {msg}", file=sys.stderr, flush=True)
+
+
+def tables_both(pk, wl, share=True):
+    tc = synth.build_tables(pk.Allocator, wl, share=share)
+    tr = synth.build_tables(RefAllocator, wl, share=share)
+    for name in tc:
+        np.testing.assert_array_equal(tc[name]["tables"], tr[name]["tables"])
+        for x, y in zip(tc[name]["step_slots"], tr[name]["step_slots"]):
+            np.testing.assert_array_equal(x, y)
+    return tc, tr
+
+
+def pool_bits(t):
+    """Device pool -> float32 bit patterns (bf16 upcasts exactly)."""
+    import torch
+
+    return t.float().cpu().numpy().view(np.uint32) if t.dtype != torch.float32 else \
+        t.cpu().numpy().view(np.uint32)
+
+
+def check_attention(wl, outs, ref, rows=None, label=""):
+    for name, o in outs.items():
+        max_abs, rel = runner.compare(o, ref[name], wl.dtype, rows)
+        assert np.all(np.isfinite(o.float().cpu().numpy()[rows] if rows is not None else o.float().cpu().numpy()))
+        assert runner.within(wl.dtype, max_abs, rel), f"{label}/{name}: max_abs={max_abs:.3g} rel_l2={rel:.3g}"
+
+
+def run_case(pk, wl, rows=None, label="", **step_kw):
+    announce(f"{label} {wl.name} B={wl.batch} Hq={wl.hq} Hkv={wl.hkv} D={wl.head_dim} {wl.dtype} "
+             f"lens={wl.seq_lens[:8].tolist()}")
+    tc, tr = tables_both(pk, wl)
+    dev = runner.gpu_setup(wl, tc)
+    ws = runner.gpu_workspace(wl, dev, step_kw.get("partition_tokens"), step_kw.get("max_seq_len"))
+    outs = runner.gpu_step(wl, dev, workspace=ws, **step_kw)
+    import torch
+
+    torch.cuda.synchronize()
+    pools = runner.oracle_setup(wl, tr)
+    ref = runner.oracle_step(wl, pools, rows=rows)
+    check_attention(wl, outs, ref, rows, label)
+    return wl, tc, dev, outs, pools
+
+
+# --------------------------------------------------------------- write/gather
+@pytest.mark.parametrize("name,kw", [
+    ("tiny", {}),
+    ("qwen3", dict(context=300, prefix=64, num_blocks=200)),
+    ("hybrid", dict(batch=3, context=700, window=64, sliding_blocks=40, num_blocks=200)),
+    ("prefill", dict(batch=3, context=[70, 33, 0], chunk=[40, 9, 17], num_blocks=64)),
+    ("mixed", dict(batch=5, context=(20, 300), prefix=100, num_blocks=200, head_dim=256, hq=4, hkv=2)),
+])
+def test_write_is_bit_exact(pk, name, kw):
+    import torch
+
+    wl = synth.make(name, **kw)
+    announce(f"write {name}")
+    tc, tr = tables_both(pk, wl)
+    dev = runner.gpu_setup(wl, tc)
+    runner.gpu_step(wl, dev, workspace=runner.gpu_workspace(wl, dev))
+    torch.cuda.synchronize()
+    pools = runner.oracle_setup(wl, tr)
+    for L in wl.layers:
+        if L.alias_of:
+            continue
+        kp, vp, _ = pools[L.name]
+        np.testing.assert_array_equal(pool_bits(dev[L.name]["k_pool"]), kp.view(np.uint32))
+        np.testing.assert_array_equal(pool_bits(dev[L.name]["v_pool"]), vp.view(np.uint32))
+
+
+def test_write_skips_padding_and_out_of_range_slots(pk):
+    import torch
+
+    announce("write padding")
+    kp = torch.full((4, 2, 16, 64), float("nan"), device="cuda")
+    vp = torch.full_like(kp, float("nan"))
+    new = torch.arange(5 * 2 * 64, dtype=torch.float32, device="cuda").reshape(5, 2, 64)
+    slots = torch.tensor([17, -1, 4 * 16, 63, -5], dtype=torch.int64, device="cuda")
+    pk.paged_kv_write(kp, vp, new, -new, slots)
+    k = kp.cpu()
+    assert torch.equal(k[1, :, 1], new[0].cpu()) and torch.equal(k[3, :, 15], new[3].cpu())
+    assert int(torch.isnan(k).sum()) == (4 * 16 - 2) * 2 * 64
+    assert torch.equal(vp.cpu()[1, :, 1], -new[0].cpu())
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("tiny", {}),
+    ("mixed", dict(batch=6, context=(20, 300), prefix=100, num_blocks=300)),
+    ("hybrid", dict(batch=3, context=700, window=64, sliding_blocks=40, num_blocks=200)),
+])
+def test_gather_returns_flat_kv(pk, name, kw):
+    import torch
+
+    wl = synth.make(name, **kw)
+    announce(f"gather {name}")
+    tc, _ = tables_both(pk, wl)
+    dev = runner.gpu_setup(wl, tc)
+    runner.gpu_step(wl, dev, workspace=runner.gpu_workspace(wl, dev))
+    for L in wl.layers:
+        if L.alias_of:
+            continue
+        spans, offs = [], [0]
+        for b in range(wl.batch):
+            n = int(wl.seq_lens[b])
+            lo = max(0, n - L.window) if L.window else 0
+            spans.append((lo, n))
+            offs.append(offs[-1] + n - lo)
+        total = offs[-1]
+        ok = torch.empty((total, wl.hkv, wl.head_dim), dtype=dev[L.name]["k_pool"].dtype, device="cuda")
+        ov = torch.empty_like(ok)
+        pk.paged_kv_gather(ok, ov, dev[L.name]["k_pool"], dev[L.name]["v_pool"], dev[L.name]["tables"],
+                           dev["_seq_lens"], torch.tensor(offs[:-1], dtype=torch.int64, device="cuda"),
+                           wl.max_seq_len, sliding_window=L.window)
+        exp_k = np.concatenate([synth.kv_rows(wl, L, b, "k", lo, n) for b, (lo, n) in enumerate(spans)])
+        exp_v = np.concatenate([synth.kv_rows(wl, L, b, "v", lo, n) for b, (lo, n) in enumerate(spans)])
+        np.testing.assert_array_equal(pool_bits(ok), exp_k.view(np.uint32))
+        np.testing.assert_array_equal(pool_bits(ov), exp_v.view(np.uint32))
+
+
+# --------------------------------------------------------------- decode parity
+DECODE_SMALL = [
+    ("tiny", {}, {}),
+    ("tiny", dict(dtype="bf16"), {}),
+    ("tiny", {}, dict(partition_tokens=16)),
+    ("qwen3", dict(context=300, prefix=64, num_blocks=200), {}),
+    ("qwen3", dict(context=300, prefix=64, num_blocks=200), dict(partition_tokens=64)),
+    ("mixed", dict(batch=7, context=(1, 700), prefix=200, num_blocks=400), dict(partition_tokens=128)),
+    ("mixed", dict(batch=5, hq=16, hkv=1, context=(100, 600), prefix=64, num_blocks=300), {}),
+    ("mixed", dict(batch=5, hq=6, hkv=1, context=(100, 600), prefix=64, num_blocks=300), dict(partition_tokens=64)),
+    ("mixed", dict(batch=5, hq=6, hkv=2, head_dim=64, context=(1, 300), prefix=32, num_blocks=200), {}),
+    ("mixed", dict(batch=4, hq=8, hkv=8, head_dim=256, context=(30, 400), prefix=48, num_blocks=200), dict(partition_tokens=32)),
+    ("mixed", dict(batch=4, hq=8, hkv=2, head_dim=128, dtype="f32", context=(30, 400), prefix=48, num_blocks=200), {}),
+    ("mixed", dict(batch=4, hq=4, hkv=2, head_dim=256, dtype="f32", context=(30, 200), prefix=48, num_blocks=100), dict(partition_tokens=48)),
+    ("hybrid", dict(batch=3, context=700, window=64, sliding_blocks=40, num_blocks=200), {}),
+    ("hybrid", dict(batch=3, context=700, window=1, sliding_blocks=40, num_blocks=200), {}),
+    ("hybrid", dict(batch=2, context=300, window=100, hq=4, hkv=2, head_dim=128, sliding_blocks=40, num_blocks=100), dict(partition_tokens=32)),
+]
+
+
+@pytest.mark.parametrize("name,kw,step", DECODE_SMALL,
+                         ids=[f"{n}-{i}" for i, (n, _, _) in enumerate(DECODE_SMALL)])
+def test_decode_small(pk, name, kw, step):
+    run_case(pk, synth.make(name, **kw), label="decode-small", **step)
+
+
+@pytest.mark.parametrize("name", ["tiny", "qwen3", "mixed", "hybrid"])
+def test_decode_full_size(pk, name):
+    run_case(pk, synth.make(name), label="decode-full")
+
+
+def test_decode_edge_lengths(pk):
+    # a 1-token row and a row one past a block boundary, full and sliding
+    run_case(pk, synth.make("tiny", context=[1, 17], prefix=0), label="edge-1-17")
+    run_case(pk, synth.make("tiny", context=[16, 33], prefix=16), label="edge-16-33",
+             partition_tokens=16)
+
+
+def test_decode_empty_row_gives_zeros(pk):
+    import torch
+
+    announce("decode empty row")
+    wl = synth.make("tiny", context=[40, 75])
+    tc, _ = tables_both(pk, wl)
+    dev = runner.gpu_setup(wl, tc)
+    dev["_seq_lens"][0] = 0
+    for part in (0, 16):
+        ws = runner.gpu_workspace(wl, dev, part)
+        outs = runner.gpu_step(wl, dev, workspace=ws, partition_tokens=part)
+        assert torch.all(outs["main"][0] == 0)
+        assert torch.all(torch.isfinite(outs["main"][1]))
+
+
+def _outputs(pk, wl, share=True, **step):
+    tc = synth.build_tables(pk.Allocator, wl, share=share)
+    dev = runner.gpu_setup(wl, tc)
+    ws = runner.gpu_workspace(wl, dev, step.get("partition_tokens"), step.get("max_seq_len"))
+    outs = runner.gpu_step(wl, dev, workspace=ws, **step)
+    return {k: v.cpu() for k, v in outs.items()}
+
+
+def test_decode_invariances_bit_exact(pk):
+    import torch
+
+    announce("decode invariances")
+    kw = dict(batch=6, context=(50, 900), prefix=300, num_blocks=600)
+    base = _outputs(pk, synth.make("mixed", **kw))["main"]
+    # determinism
+    assert torch.equal(base, _outputs(pk, synth.make("mixed", **kw))["main"])
+    # physical placement does not matter
+    wl = synth.make("mixed", **kw)
+    wl.layers[0].free_order = np.random.default_rng(99).permutation(np.arange(1, 600)).astype(np.int32)
+    assert torch.equal(base, _outputs(pk, wl)["main"])
+    # shared prefix blocks == private copies of the same data
+    assert torch.equal(base, _outputs(pk, synth.make("mixed", **kw), share=False)["main"])
+    # extra (empty) partitions from a larger max_seq_len change nothing
+    assert torch.equal(base, _outputs(pk, synth.make("mixed", **kw), max_seq_len=4000)["main"])
+    # a row's result does not depend on the other rows of the batch
+    sub = synth.make("mixed", **kw)
+    sub.batch = 1
+    sub.seq_lens = sub.seq_lens[:1].copy()
+    sub.tokens = sub.tokens[:1]
+    L = sub.layers[0]
+    L.q, L.k, L.v, L.live_from = L.q[:1], L.k[:1], L.v[:1], L.live_from[:1]
+    assert torch.equal(base[0], _outputs(pk, sub)["main"][0])
+
+
+def test_decode_partition_sizes_agree(pk):
+    import torch
+
+    announce("decode partition sizes")
+    kw = dict(batch=4, context=(300, 900), prefix=100, num_blocks=300, dtype="f32", hq=8, hkv=2)
+    outs = [_outputs(pk, synth.make("mixed", **kw), partition_tokens=p)["main"] for p in (16, 64, 512, 1024)]
+    for o in outs[1:]:
+        assert float((o - outs[0]).abs().max()) <= 1e-6
+
+
+# --------------------------------------------------------------- prefill parity
+PREFILL_SMALL = [
+    dict(batch=1, context=[0], chunk=[1], num_blocks=16),
+    dict(batch=3, context=[70, 33, 0], chunk=[40, 9, 17], num_blocks=64),
+    dict(batch=2, context=[300, 5], chunk=[200, 130], num_blocks=64),
+    dict(batch=2, context=[100, 64], chunk=[64, 100], num_blocks=64, hq=8, hkv=8),
+    dict(batch=2, context=[100, 64], chunk=[64, 100], num_blocks=64, hq=6, hkv=1),
+    dict(batch=2, context=[100, 64], chunk=[64, 100], num_blocks=64, hq=16, hkv=2, head_dim=64),
+    dict(batch=2, context=[100, 64], chunk=[64, 100], num_blocks=64, hq=4, hkv=1, head_dim=256),
+    dict(batch=2, context=[300, 64], chunk=[150, 100], num_blocks=64, window=37),
+    dict(batch=1, context=[500], chunk=[129], num_blocks=64, window=200, hq=4, hkv=4),
+]
+
+
+@pytest.mark.parametrize("kw", PREFILL_SMALL, ids=[str(i) for i in range(len(PREFILL_SMALL))])
+def test_prefill_small(pk, kw):
+    run_case(pk, synth.make("prefill", **kw), label="prefill-small")
+
+
+def test_prefill_full_size_sampled_rows(pk):
+    wl = synth.make("prefill")
+    rows = sorted(set([0, 1, 2, 31, 32, 127, 128, 1000, 1023, 1024, 2046, 2047] +
+                      list(np.random.default_rng(5).integers(0, 2048, size=40))))
+    run_case(pk, wl, rows=rows, label="prefill-full")
+
+
+def test_prefill_chunk_of_one_matches_decode(pk):
+    import torch
+
+    announce("prefill C=1 vs decode")
+    wl = synth.make("prefill", batch=2, context=[77, 300], chunk=[1, 1], num_blocks=64)
+    tc, _ = tables_both(pk, wl)
+    dev = runner.gpu_setup(wl, tc)
+    pre = runner.gpu_step(wl, dev)["main"]
+    out = torch.empty_like(pre)
+    d = dev["main"]
+    pk.paged_attn_decode(out, d["q"], d["k_pool"], d["v_pool"], d["tables"], dev["_seq_lens"], wl.scale,
+                         wl.max_seq_len, partition_tokens=1024)
+    assert float((pre.float() - out.float()).abs().max()) <= 2e-2

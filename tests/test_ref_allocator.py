@@ -37,11 +37,11 @@ def run_script(make, steps):
         elif op == "reserve":
             a.reserve(st["seq"], st["tokens"])
         elif op == "reserve_fail":
-            before = (a.num_free(), a.block_tables([st["seq"]], 64))
+            before = (a.num_free(), [list(map(int, r)) for r in a.block_tables([st["seq"]], 64)])
             with pytest.raises(Exception) as ei:
                 a.reserve(st["seq"], st["tokens"])
             assert ei.value.code == st["code"], where
-            assert (a.num_free(), a.block_tables([st["seq"]], 64)) == before, where
+            assert (a.num_free(), [list(map(int, r)) for r in a.block_tables([st["seq"]], 64)]) == before, where
         elif op == "commit":
             a.commit_tokens(st["seq"], st["tokens"])
         elif op == "publish":
