@@ -33,10 +33,12 @@ import time
 import numpy as np
 
 METRIC = "paged decode attn: KV GB/s & % HBM peak; prefill-chunk TFLOP/s & % MFMA"
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = {"decode_partial": ["decode.hip", "device.h"], "prefill": ["prefill.hip", "device.h"]}
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 DEFAULT_WAVES = {"qwen3": 16}
-DEFAULT_STEPS = {"qwen3": 400, "mixed": 100, "hybrid": 100, "prefill": 20, "tiny": 200}
+DEFAULT_STEPS = {"qwen3": 1000, "mixed": 200, "hybrid": 200, "prefill": 30, "tiny": 500}
 
 
 def log(msg):
@@ -98,6 +100,38 @@ def prefill_flops(wl, rows=None):
     return 4.0 * wl.head_dim * wl.hq * pairs
 
 
+def source_hash(kern):
+    """sha256 of the source files a kernel is built from."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kern]:
+        with open(os.path.join(ROOT, "block_paged_kv_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def counter_traffic(kern, workload):
+    """HBM bytes per launch recorded in profiles/<kern>_<workload>_hbm_counters.md
+    (FETCH_SIZE and WRITE_SIZE, scaled by a copy of known size), or None when
+    the file is missing or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{kern}_{workload}_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and line.lstrip().startswith("- `"):
+                k, v = line.split(":", 1)
+                fields[k.strip(" -`")] = v.strip(" `\n")
+    if fields.get("source_sha256") != source_hash(kern):
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -146,6 +180,21 @@ def cpu_baseline(wl, args):
                       f"(BLAS threads {blas_threads()})"}
 
 
+def copy_calibration():
+    """A plain device-to-device copy of a known size, launched 5 times, so the
+    HBM byte counters (FETCH_SIZE, WRITE_SIZE) of the kernels above can be
+    scaled by what the same counters read for known traffic."""
+    import torch
+
+    nbytes = 256 << 20
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 5}), flush=True)
+
+
 def _subset(wl, rows):
     import copy
 
@@ -170,8 +219,14 @@ def main():
     ap.add_argument("--waves", type=int, default=None, help="independent batches rotated through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 256 MiB device copy (scales HBM byte counters)")
     args = ap.parse_args()
 
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; a multi-GPU run is not available "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
@@ -195,7 +250,9 @@ def main():
     dev = runner.gpu_setup(wl, tabs, fill=0.0)
     torch.cuda.synchronize()
 
-    # Prepared calls for every step variant (one per wave).
+    # Prepared calls for every step variant (one per wave), bound to a stream
+    # of our own so they can be captured into a graph.
+    stream = torch.cuda.Stream()
     calls = []
     if wl.kind == "decode":
         outs = {L.name: torch.empty((wsz,) + tuple(dev[L.name]["q"].shape[1:]), dtype=dev[L.name]["q"].dtype,
@@ -214,7 +271,7 @@ def main():
             t0 = sum(nt[:r * wsz])
             t1 = sum(nt[:(r + 1) * wsz])
             seq.append(pk.paged_kv_write(d["k_pool"], d["v_pool"], d["step_k"][t0:t1], d["step_v"][t0:t1],
-                                         d["step_slots"][t0:t1], prepare=True))
+                                         d["step_slots"][t0:t1], stream=stream, prepare=True))
         for L in wl.layers:
             d = dev[L.name]
             if wl.kind == "decode":
@@ -222,33 +279,67 @@ def main():
                     outs[L.name], d["q"][rows], d["k_pool"], d["v_pool"], d["tables"][rows],
                     dev["_seq_lens"][rows], wl.scale, int(wl.seq_lens[rows].max()),
                     sliding_window=L.window, partition_tokens=wl.partition_tokens, workspace=ws,
-                    prepare=True))
+                    stream=stream, prepare=True))
             else:
                 seq.append(pk.paged_attn_prefill_chunk(
                     outs[L.name], d["q"], d["k_pool"], d["v_pool"], d["tables"], dev["_cu_q"],
                     dev["_seq_lens"], int(wl.chunk_lens.max()), wl.scale, sliding_window=L.window,
-                    prepare=True))
+                    stream=stream, prepare=True))
         calls.append(seq)
 
     def step(i):
         for c in calls[i % R]:
             c()
 
+    stream.wait_stream(torch.cuda.current_stream())
     log(f"[bench] warmup {args.warmup} steps")
-    for i in range(args.warmup):
-        step(i)
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step(i)
     torch.cuda.synchronize()
-    pk.trace_reset()
-    pk.trace_enable(True)
+
+    # Timed region 1 (throughput): `steps` consecutive steps captured as one
+    # HIP graph, so host launch overhead is not part of a step. Falls back to
+    # eager launches if capture is not possible.
+    timing = "graph"
+    graph = None
+    if not args.eager:
+        try:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                for i in range(steps):
+                    step(args.warmup + i)
+            graph.replay()  # warm replay: instantiation and first-touch costs
+            torch.cuda.synchronize()
+        except Exception as e:  # noqa: BLE001
+            log(f"[bench] graph capture failed ({e}); timing eager launches")
+            graph = None
+            timing = "eager"
+    log(f"[bench] timing {steps} steps ({timing})")
     torch.cuda.synchronize()
-    log(f"[bench] timing {steps} steps")
     t0 = time.perf_counter()
-    for i in range(steps):
-        step(args.warmup + i)
+    if graph is not None:
+        graph.replay()
+    else:
+        with torch.cuda.stream(stream):
+            for i in range(steps):
+                step(args.warmup + i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    pk.trace_enable(False)
     ms_per_step = (t1 - t0) * 1e3 / steps
+
+    # Timed region 2 (per-kernel durations): the same steps launched eagerly,
+    # the library recording a HIP event pair around every launch on the launch
+    # stream (events inside a captured graph cannot be timed).
+    log(f"[bench] per-kernel timing over {steps} eager steps")
+    pk.trace_reset()
+    torch.cuda.synchronize()
+    pk.trace_enable(True)
+    with torch.cuda.stream(stream):
+        for i in range(steps):
+            step(args.warmup + i)
+    torch.cuda.synchronize()
+    pk.trace_enable(False)
 
     if wl.kind == "decode":
         per_wave = [decode_bytes(wl, tabs, list(range(r * wsz, (r + 1) * wsz))) for r in range(R)]
@@ -272,6 +363,11 @@ def main():
         ms, n = pk.trace_query(name)
         if n:
             kernels[name] = {"launches": n, "avg_us": round(ms * 1e3 / n, 3)}
+    if wl.kind == "decode" and len(wl.layers) > 1:
+        # partial launches cycle through the layers in order within a step
+        dur = pk.trace_durations("decode_partial")
+        kernels["decode_partial_by_layer_avg_us"] = {
+            L.name: round(float(np.mean(dur[i::len(wl.layers)])) * 1e3, 3) for i, L in enumerate(wl.layers)}
     log(f"[bench] kernels: {kernels}")
 
     result = {
@@ -303,12 +399,13 @@ def main():
             "peak": peak,
             "unit": runit,
             "frac": round(achieved / peak, 4),
-            "traffic": None,
+            "traffic": counter_traffic(kern, args.workload),
             "avg_launch_us": round(k_ms * 1e3 / max(k_n, 1), 3),
             "launches": k_n,
             "work_per_step": work,
         },
         "kernels": kernels,
+        "timing": timing,
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")

@@ -72,6 +72,7 @@ _SIGNATURES = {
     "paged_trace_enable": [_c_int32],
     "paged_trace_reset": [],
     "paged_trace_query": [_c_int32, ctypes.POINTER(ctypes.c_double), _P_I64],
+    "paged_trace_durations": [_c_int32, ctypes.POINTER(ctypes.c_double), _c_int64, _P_I64],
     "paged_alloc_create": [_c_int32, _c_int32, _P_I32, ctypes.POINTER(_c_void_p)],
     "paged_alloc_destroy": [_c_void_p],
     "paged_alloc_grow": [_c_void_p, _c_int32, _P_I32],
@@ -93,9 +94,17 @@ _SIGNATURES = {
 
 
 def _load():
+    # torch wheels ship their own HIP runtime under the same soname as the
+    # system one. Importing torch first makes the library bind to that
+    # already-loaded runtime, so the process holds exactly one HIP runtime
+    # (loading the library first would let torch bring in a second one).
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is not built; run `python -m block_paged_kv_amd.build` "
+            f"{LIB_PATH} is not built; run `python block_paged_kv_amd/build.py` "
             "(the HIP library is required: there is no fallback path)")
     lib = ctypes.CDLL(LIB_PATH)
     for name, argtypes in _SIGNATURES.items():
@@ -279,6 +288,17 @@ def trace_query(kernel):
     n = ctypes.c_int64()
     _check(lib.paged_trace_query(KERNELS[kernel], ctypes.byref(ms), ctypes.byref(n)))
     return ms.value, n.value
+
+
+def trace_durations(kernel):
+    """Per-launch durations (ms, numpy float64) recorded for ``kernel``, in launch order."""
+    n = ctypes.c_int64()
+    _check(lib.paged_trace_durations(KERNELS[kernel], None, 0, ctypes.byref(n)))
+    out = np.zeros(n.value, dtype=np.float64)
+    if n.value:
+        _check(lib.paged_trace_durations(KERNELS[kernel], out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+                                         n.value, ctypes.byref(n)))
+    return out
 
 
 # ------------------------------------------------------------------ allocator

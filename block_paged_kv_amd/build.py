@@ -1,6 +1,7 @@
 """Build libpagedkv.so in-tree: HIP sources with hipcc for gfx950, host C++ with g++.
 
-Usage: ``python -m block_paged_kv_amd.build`` (or ``build()`` from Python).
+Usage: ``python block_paged_kv_amd/build.py`` (run the file, not the module:
+importing the package loads the library this script builds).
 Every call recompiles every source, so the library always matches the tree.
 """
 

@@ -104,8 +104,8 @@ extern "C" int32_t paged_kv_write(void* k_pool, void* v_pool, const void* new_k,
   const int64_t blocks = std::min<int64_t>((total + kThreads - 1) / kThreads, 16384);
   hipStream_t s = static_cast<hipStream_t>(stream);
   LaunchTrace tr(PAGED_KERNEL_KV_WRITE, s);
-  kv_write_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s>>>(
-      static_cast<uint4*>(k_pool), static_cast<uint4*>(v_pool), static_cast<const uint4*>(new_k),
+  hipExtLaunchKernelGGL(kv_write_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s,
+      tr.start(), tr.stop(), 0, static_cast<uint4*>(k_pool), static_cast<uint4*>(v_pool), static_cast<const uint4*>(new_k),
       static_cast<const uint4*>(new_v), slot_mapping, total, vecs_per_token, vecs_per_head,
       num_kv_heads, ilog2(block_size), static_cast<int64_t>(num_blocks) * block_size);
   tr.finish();
@@ -135,8 +135,8 @@ extern "C" int32_t paged_kv_gather(void* out_k, void* out_v, const void* k_pool,
   const int64_t gx = std::min<int64_t>((per_row + kThreads - 1) / kThreads, 4096);
   hipStream_t s = static_cast<hipStream_t>(stream);
   LaunchTrace tr(PAGED_KERNEL_KV_GATHER, s);
-  kv_gather_kernel<<<dim3(static_cast<unsigned>(gx), static_cast<unsigned>(batch)), dim3(kThreads),
-                     0, s>>>(static_cast<uint4*>(out_k), static_cast<uint4*>(out_v),
+  hipExtLaunchKernelGGL(kv_gather_kernel, dim3(static_cast<unsigned>(gx), static_cast<unsigned>(batch)),
+                        dim3(kThreads), 0, s, tr.start(), tr.stop(), 0, static_cast<uint4*>(out_k), static_cast<uint4*>(out_v),
                              static_cast<const uint4*>(k_pool), static_cast<const uint4*>(v_pool),
                              block_tables, max_blocks_per_seq, seq_lens, out_offsets, max_seq_len,
                              vecs_per_token, vecs_per_head, num_kv_heads, ilog2(block_size),

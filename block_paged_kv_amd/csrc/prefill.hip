@@ -60,7 +60,7 @@ __device__ __forceinline__ floatx4_t mfma16x16x32(const uint4& a, const uint4& b
 }
 
 template <int D>
-__global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillParams a) {
+__global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillParams a) {
   constexpr int KSTR = D + 8;        // K row stride in LDS (elements): spreads banks
   constexpr int VSTR = kTileN + 8;   // V^T row stride in LDS (elements)
   constexpr int DCH = D / 8;         // 16-byte chunks per key row
@@ -68,8 +68,8 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillParams a) {
   constexpr int NT = D / 16;         // output column tiles
   constexpr float kNegInf = -INFINITY;
 
-  __shared__ __attribute__((aligned(16))) uint16_t k_s[kTileN * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_s[D * VSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t k_s[2][kTileN * KSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t vt_s[2][D * VSTR];
 
   // XCD-aware work mapping: XCD x takes work items [x*per_xcd, (x+1)*per_xcd).
   const int lin = blockIdx.x;
@@ -123,68 +123,128 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillParams a) {
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) o[j][nt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  float m[2] = {kNegInf, kNegInf};
-  float l[2] = {0.f, 0.f};
+  float m[2] = {kNegInf, kNegInf};   // running max of raw scores
+  float l[2] = {0.f, 0.f};           // this lane's share of the running sum
 
   const int32_t* bt = a.bt + static_cast<size_t>(b) * a.mb;
-  const int bs_mask = (1 << a.bs_log2) - 1;
+  const int bs_log2 = a.bs_log2;
+  const int bs_mask = (1 << bs_log2) - 1;
   const int kt_begin = lo_min / kTileN;
   const int kt_end = a_max / kTileN;  // inclusive
+  const int tile_blocks = kTileN >> bs_log2;  // blocks per K/V tile (block_size <= 64)
+  const float c = a.scale_log2;
+
+  // Block-table entries of one tile, one per lane (lane < tile_blocks).
+  auto load_entries = [&](int kt) -> int {
+    const int lb = ((kt * kTileN) >> bs_log2) + lane;
+    return (kt <= kt_end && lane < tile_blocks && lb < a.mb && (lb << bs_log2) < n) ? bt[lb] : 0;
+  };
+  auto phys_ok = [&](int phys) { return phys > 0 && phys < a.nb; };
+
+  // Staging: wave w moves keys 16w .. 16w+15 of a tile (one block when
+  // block_size >= 16, so its base address is wave-uniform). K: lane l copies
+  // 16-byte chunk l % DCH of keys 16w + (64/DCH)*i + l / DCH. V: lane l owns
+  // the 4 keys 16w + 4*(l % 4) .. +3 and 16-byte chunk l / 4 (+16*i), which it
+  // writes transposed.
+  constexpr int KROWS = 64 / DCH;                 // keys one K load instruction covers
+  constexpr int KI = 16 / KROWS;                  // K loads per lane per tile
+  constexpr int VI = (DCH + 15) / 16;             // V units per lane per tile
+  uint4 kreg[KI];
+  uint4 vreg[VI][4];
+  const int k_key = wave * 16 + lane / DCH;       // + KROWS * i
+  const int k_dc = lane % DCH;
+  const int v_key = wave * 16 + 4 * (lane & 3);   // + e
+  const int v_dc = lane >> 2;                     // + 16 * i
+  // Physical block of key `key` of tile kt, from the tile's entries `ent`.
+  auto block_of = [&](int ent, int key) { return __shfl(ent, key >> bs_log2); };
+  auto row_ptr = [&](const uint16_t* pool, int phys, int kp) {
+    return pool + (((static_cast<size_t>(phys) * a.hkv + kvh) << bs_log2) + (kp & bs_mask)) * D;
+  };
+  auto stage_load = [&](int kt, int ent) {
+    const int ts = kt * kTileN;
+    // Fast path: every key of the tile exists and every block id is valid.
+    const bool full = ts + kTileN <= n && __all(lane >= tile_blocks || phys_ok(ent));
+    if (full) {
+#pragma unroll
+      for (int i = 0; i < KI; ++i) {
+        const int key = k_key + KROWS * i;
+        kreg[i] = *reinterpret_cast<const uint4*>(row_ptr(a.k_pool, block_of(ent, key), ts + key) + k_dc * 8);
+      }
+#pragma unroll
+      for (int i = 0; i < VI; ++i) {
+        const int phys = block_of(ent, v_key);
+        if (v_dc + 16 * i < DCH) {  // always true unless head_dim == 64
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            vreg[i][e] = *reinterpret_cast<const uint4*>(row_ptr(a.v_pool, phys, ts + v_key + e) +
+                                                        (v_dc + 16 * i) * 8);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < KI; ++i) {
+        const int key = k_key + KROWS * i;
+        const int phys = block_of(ent, key);
+        kreg[i] = make_uint4(0, 0, 0, 0);
+        if (ts + key < n && phys_ok(phys))
+          kreg[i] = *reinterpret_cast<const uint4*>(row_ptr(a.k_pool, phys, ts + key) + k_dc * 8);
+      }
+#pragma unroll
+      for (int i = 0; i < VI; ++i) {
+        const int phys = block_of(ent, v_key);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          vreg[i][e] = make_uint4(0, 0, 0, 0);
+          if (v_dc + 16 * i < DCH && ts + v_key + e < n && phys_ok(phys))
+            vreg[i][e] = *reinterpret_cast<const uint4*>(row_ptr(a.v_pool, phys, ts + v_key + e) +
+                                                        (v_dc + 16 * i) * 8);
+        }
+      }
+    }
+  };
+  // Registers -> LDS buffer `buf`: K row-major, V transposed.
+  auto stage_store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < KI; ++i)
+      *reinterpret_cast<uint4*>(&k_s[buf][(k_key + KROWS * i) * KSTR + k_dc * 8]) = kreg[i];
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+      const int dc = v_dc + 16 * i;
+      if (dc < DCH) {
+        const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vreg[i][0]);
+        const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vreg[i][1]);
+        const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vreg[i][2]);
+        const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vreg[i][3]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // element 2e: low halves of the 4 keys; element 2e+1: high halves
+          uint2 lo2, hi2;
+          lo2.x = __builtin_amdgcn_perm(w1[e], w0[e], 0x05040100u);
+          lo2.y = __builtin_amdgcn_perm(w3[e], w2[e], 0x05040100u);
+          hi2.x = __builtin_amdgcn_perm(w1[e], w0[e], 0x07060302u);
+          hi2.y = __builtin_amdgcn_perm(w3[e], w2[e], 0x07060302u);
+          *reinterpret_cast<uint2*>(&vt_s[buf][(dc * 8 + 2 * e) * VSTR + v_key]) = lo2;
+          *reinterpret_cast<uint2*>(&vt_s[buf][(dc * 8 + 2 * e + 1) * VSTR + v_key]) = hi2;
+        }
+      }
+    }
+  };
+
+  int ent_next = load_entries(kt_begin + 1);
+  stage_load(kt_begin, load_entries(kt_begin));
+  stage_store(0);
+  __syncthreads();
 
   for (int kt = kt_begin; kt <= kt_end; ++kt) {
+    const int buf = (kt - kt_begin) & 1;
+    const bool has_next = kt < kt_end;
+    if (has_next) {  // tile kt+1 streams into registers while tile kt computes
+      stage_load(kt + 1, ent_next);
+      ent_next = load_entries(kt + 2);
+    }
     const int ts = kt * kTileN;
-    __syncthreads();  // previous tile fully consumed
-    // ---- stage K (row-major) -------------------------------------------------
-    for (int c = tid; c < kTileN * DCH; c += kWaves * 64) {
-      const int key = c / DCH;
-      const int dc = c - key * DCH;
-      const int kp = ts + key;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (kp < n) {
-        const int lb = kp >> a.bs_log2;
-        const int phys = lb < a.mb ? bt[lb] : 0;
-        if (phys > 0 && phys < a.nb) {
-          const size_t row = ((static_cast<size_t>(phys) * a.hkv + kvh) << a.bs_log2) + (kp & bs_mask);
-          v = *reinterpret_cast<const uint4*>(a.k_pool + row * D + dc * 8);
-        }
-      }
-      *reinterpret_cast<uint4*>(&k_s[key * KSTR + dc * 8]) = v;
-    }
-    // ---- stage V transposed: unit = 4 keys x 8 head_dim elements -------------
-    for (int u = tid; u < (kTileN / 4) * DCH; u += kWaves * 64) {
-      const int kg = u % (kTileN / 4);
-      const int dc = u / (kTileN / 4);
-      uint4 w[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kp = ts + kg * 4 + i;
-        w[i] = make_uint4(0, 0, 0, 0);
-        if (kp < n) {
-          const int lb = kp >> a.bs_log2;
-          const int phys = lb < a.mb ? bt[lb] : 0;
-          if (phys > 0 && phys < a.nb) {
-            const size_t row = ((static_cast<size_t>(phys) * a.hkv + kvh) << a.bs_log2) + (kp & bs_mask);
-            w[i] = *reinterpret_cast<const uint4*>(a.v_pool + row * D + dc * 8);
-          }
-        }
-      }
-      const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&w[0]);
-      const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&w[1]);
-      const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&w[2]);
-      const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&w[3]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // head_dim element 2e: low halves; 2e+1: high halves (keys 0..3 in order)
-        uint2 lo2, hi2;
-        lo2.x = __builtin_amdgcn_perm(w1[e], w0[e], 0x05040100u);
-        lo2.y = __builtin_amdgcn_perm(w3[e], w2[e], 0x05040100u);
-        hi2.x = __builtin_amdgcn_perm(w1[e], w0[e], 0x07060302u);
-        hi2.y = __builtin_amdgcn_perm(w3[e], w2[e], 0x07060302u);
-        *reinterpret_cast<uint2*>(&vt_s[(dc * 8 + 2 * e) * VSTR + kg * 4]) = lo2;
-        *reinterpret_cast<uint2*>(&vt_s[(dc * 8 + 2 * e + 1) * VSTR + kg * 4]) = hi2;
-      }
-    }
-    __syncthreads();
+    const uint16_t* ks_buf = k_s[buf];
+    const uint16_t* vs_buf = vt_s[buf];
 
     // ---- S^T = K Q^T : 4 key sub-tiles x 2 query tiles ----------------------
     floatx4_t s[2][4];
@@ -196,7 +256,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillParams a) {
     for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const uint4 ka = *reinterpret_cast<const uint4*>(&k_s[(t4 * 16 + lq) * KSTR + ks * 32 + lg * 8]);
+        const uint4 ka = *reinterpret_cast<const uint4*>(&ks_buf[(t4 * 16 + lq) * KSTR + ks * 32 + lg * 8]);
 #pragma unroll
         for (int j = 0; j < 2; ++j) s[j][t4] = mfma16x16x32(ka, qreg[j][ks], s[j][t4]);
       }
@@ -206,32 +266,41 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillParams a) {
     uint4 pa[2][2];  // P as bf16 A operands: [query tile][32-key step]
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
+      if (need_mask) {
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int kp = ts + t4 * 16 + lg * 4 + i;
+            if (!(kp >= qlo[j] && kp <= qpos[j] && qvalid[j])) s[j][t4][i] = kNegInf;
+          }
+      }
       float mx = kNegInf;
 #pragma unroll
       for (int t4 = 0; t4 < 4; ++t4)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = s[j][t4][i] * a.scale_log2;
-          if (need_mask) {
-            const int kp = ts + t4 * 16 + lg * 4 + i;
-            if (!(kp >= qlo[j] && kp <= qpos[j] && qvalid[j])) v = kNegInf;
-          }
-          s[j][t4][i] = v;
-          mx = fmaxf(mx, v);
-        }
+        mx = fmaxf(fmaxf(mx, fmaxf(s[j][t4][0], s[j][t4][1])), fmaxf(s[j][t4][2], s[j][t4][3]));
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(m[j], mx);
-      const float mref = mnew == kNegInf ? 0.f : mnew;
-      const float alpha = fast_exp2(m[j] - mref);
-      m[j] = mnew;
+      // Lazy rescaling: keep the reference max m[j] until a score exceeds it by
+      // more than 2^8 (in log2 units); until then probabilities stay <= 256,
+      // harmless in fp32 and bf16, and the final division by the sum taken
+      // with the same reference cancels the choice exactly.
+      const bool grow = __any(mx * c > (m[j] == kNegInf ? kNegInf : m[j] * c) + 8.f);
+      float alpha = 1.f;
+      if (grow) {
+        const float mnew = fmaxf(m[j], mx);
+        const float mref = mnew == kNegInf ? 0.f : mnew;
+        alpha = fast_exp2((m[j] - mref) * c);
+        m[j] = mnew;
+      }
+      const float neg = m[j] == kNegInf ? 0.f : -m[j] * c;
       float ls = 0.f;
       float pr[4][4];
 #pragma unroll
       for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          pr[t4][i] = fast_exp2(s[j][t4][i] - mref);
+          pr[t4][i] = fast_exp2(fmaf(s[j][t4][i], c, neg));
           ls += pr[t4][i];
         }
       l[j] = l[j] * alpha + ls;
@@ -243,7 +312,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillParams a) {
         pa[j][kk].w = pack_bf16x2(pr[2 * kk + 1][2], pr[2 * kk + 1][3]);
       }
       // Rescale O rows (O layout: lane holds queries 16j + 4*lg + i).
-      if (!__all(alpha == 1.f)) {
+      if (grow) {
         float al[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * lg + i);
@@ -259,13 +328,16 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillParams a) {
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const uint16_t* vrow = &vt_s[(nt * 16 + lq) * VSTR + kk * 32 + lg * 4];
+        const uint16_t* vrow = &vs_buf[(nt * 16 + lq) * VSTR + kk * 32 + lg * 4];
         const uint2 v0 = *reinterpret_cast<const uint2*>(vrow);
         const uint2 v1 = *reinterpret_cast<const uint2*>(vrow + 16);
         const uint4 vb = make_uint4(v0.x, v0.y, v1.x, v1.y);
 #pragma unroll
         for (int j = 0; j < 2; ++j) o[j][nt] = mfma16x16x32(pa[j][kk], vb, o[j][nt]);
       }
+
+    if (has_next) stage_store(buf ^ 1);
+    __syncthreads();
   }
 
   // ---- normalise and store --------------------------------------------------
@@ -351,9 +423,12 @@ extern "C" int32_t paged_attn_prefill_chunk(void* out, const void* q, const void
   const dim3 grid(static_cast<unsigned>(prm.per_xcd * kNumXcd));
   const dim3 block(kWaves * 64);
   LaunchTrace tr(PAGED_KERNEL_PREFILL, s);
-  if (head_dim == 64) prefill_kernel<64><<<grid, block, 0, s>>>(prm);
-  else if (head_dim == 128) prefill_kernel<128><<<grid, block, 0, s>>>(prm);
-  else prefill_kernel<256><<<grid, block, 0, s>>>(prm);
+  if (head_dim == 64)
+    hipExtLaunchKernelGGL(prefill_kernel<64>, grid, block, 0, s, tr.start(), tr.stop(), 0, prm);
+  else if (head_dim == 128)
+    hipExtLaunchKernelGGL(prefill_kernel<128>, grid, block, 0, s, tr.start(), tr.stop(), 0, prm);
+  else
+    hipExtLaunchKernelGGL(prefill_kernel<256>, grid, block, 0, s, tr.start(), tr.stop(), 0, prm);
   tr.finish();
   return check_launch("paged_attn_prefill_chunk");
 }

@@ -2,6 +2,7 @@
 // argument checks.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -13,15 +14,19 @@ namespace pagedkv {
 // Compute units of the current device (cached per device); 0 on failure.
 int device_cu_count();
 
-// Records HIP events around one launch when tracing is on.
+// Timing events for one launch when tracing is on: pass start()/stop() to
+// hipExtLaunchKernelGGL, which stamps them at the kernel's own start and end
+// (host launch overhead is not included), then call finish().
 class LaunchTrace {
  public:
   LaunchTrace(int kernel, hipStream_t stream);
-  void finish();  // record the end event (call right after the launch)
+  hipEvent_t start() const { return start_; }
+  hipEvent_t stop() const { return stop_; }
+  void finish();  // keep the pair for paged_trace_query (call right after the launch)
  private:
   int kernel_;
-  hipStream_t stream_;
   hipEvent_t start_ = nullptr;
+  hipEvent_t stop_ = nullptr;
 };
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

@@ -1,5 +1,6 @@
 // Device facts, launch timing (HIP events) and launch-error reporting.
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 #include <utility>
@@ -53,14 +54,19 @@ int device_cu_count() {
   return g_cu_cache[dev];
 }
 
-LaunchTrace::LaunchTrace(int kernel, hipStream_t stream) : kernel_(kernel), stream_(stream) {
+LaunchTrace::LaunchTrace(int kernel, hipStream_t stream) : kernel_(kernel) {
   TraceStore& t = trace();
   if (!t.on.load(std::memory_order_relaxed)) return;
+  // Events inside a captured graph cannot be timed: record nothing there.
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return;
   std::lock_guard<std::mutex> lk(t.mu);
   start_ = t.get_event();
-  if (start_ && hipEventRecord(start_, stream_) != hipSuccess) {
-    t.spare.push_back(start_);
-    start_ = nullptr;
+  stop_ = t.get_event();
+  if (!start_ || !stop_) {
+    if (start_) t.spare.push_back(start_);
+    if (stop_) t.spare.push_back(stop_);
+    start_ = stop_ = nullptr;
   }
 }
 
@@ -68,15 +74,8 @@ void LaunchTrace::finish() {
   if (!start_) return;
   TraceStore& t = trace();
   std::lock_guard<std::mutex> lk(t.mu);
-  hipEvent_t end = t.get_event();
-  if (!end || hipEventRecord(end, stream_) != hipSuccess) {
-    t.spare.push_back(start_);
-    if (end) t.spare.push_back(end);
-    start_ = nullptr;
-    return;
-  }
-  t.launches[kernel_].emplace_back(start_, end);
-  start_ = nullptr;
+  t.launches[kernel_].emplace_back(start_, stop_);
+  start_ = stop_ = nullptr;
 }
 
 int32_t check_launch(const char* what) {
@@ -104,6 +103,26 @@ extern "C" int32_t paged_trace_reset(void) {
       t.spare.push_back(pr.second);
     }
     v.clear();
+  }
+  return ok();
+}
+
+extern "C" int32_t paged_trace_durations(int32_t kernel, double* ms, int64_t capacity,
+                                         int64_t* launches) {
+  if (kernel < 0 || kernel >= PAGED_KERNEL_COUNT || !launches || capacity < 0 || (capacity > 0 && !ms))
+    return fail(PAGED_ERR_INVALID_ARG, "bad argument");
+  auto& t = pagedkv::trace();
+  std::lock_guard<std::mutex> lk(t.mu);
+  const auto& v = t.launches[kernel];
+  *launches = static_cast<int64_t>(v.size());
+  const int64_t n = std::min<int64_t>(capacity, static_cast<int64_t>(v.size()));
+  for (int64_t i = 0; i < n; ++i) {
+    if (hipEventSynchronize(v[i].second) != hipSuccess)
+      return fail(PAGED_ERR_HIP, "hipEventSynchronize failed");
+    float f = 0.f;
+    if (hipEventElapsedTime(&f, v[i].first, v[i].second) != hipSuccess)
+      return fail(PAGED_ERR_HIP, "hipEventElapsedTime failed");
+    ms[i] = f;
   }
   return ok();
 }

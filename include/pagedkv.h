@@ -199,13 +199,19 @@ enum {
 };
 
 /* on != 0: from now on, every launch records a start and an end event on its
- * stream (events are created lazily; no device memory is allocated). */
+ * stream (events are created lazily; no device memory is allocated). Launches
+ * on a stream that is being captured into a graph record nothing. */
 int32_t paged_trace_enable(int32_t on);
 /* Drop all recorded launches. */
 int32_t paged_trace_reset(void);
 /* Wait for the recorded events of `kernel` and return the sum of their
- * elapsed times and the number of launches. Synchronizes those events. */
+ * elapsed times and the number of launches. Synchronizes those events. The
+ * events are stamped at the kernel's own start and end (hipExtLaunchKernel),
+ * so host launch overhead is not included. */
 int32_t paged_trace_query(int32_t kernel, double* total_ms, int64_t* launches);
+/* Per-launch durations of `kernel` in launch order: ms[i] for the first
+ * min(capacity, *launches) launches; *launches = launches recorded. */
+int32_t paged_trace_durations(int32_t kernel, double* ms, int64_t capacity, int64_t* launches);
 
 /* ----------------------------------------------------------------------
  * Host block allocator (paged-cache doc, component table: BlockAllocator)
