@@ -748,8 +748,13 @@ int32_t make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, int3
   pl->part = part;
   pl->max_parts = std::max(1, (span + part - 1) / part);
   pl->direct = pl->max_parts == 1;
+  // Waves per workgroup: long-lived waves stream best, so each wave gets at
+  // least 4 iterations of its partition (1..4 waves). The choice depends on
+  // the partition size only, so a larger max_seq_len (extra, empty
+  // partitions) never changes how a row's partials are merged.
   const int iter = iter_tokens_rt(esz, head_dim, pl->gt);
-  pl->nw = std::min(kMaxWaves, std::max(1, (part + iter - 1) / iter));
+  const int iters = (part + iter - 1) / iter;
+  pl->nw = std::min(kMaxWaves, std::max(1, iters / 4));
   pl->ws_bytes = pl->direct ? 0
                             : static_cast<size_t>(batch) * hq * pl->max_parts *
                                   (static_cast<size_t>(head_dim) + 2) * sizeof(float);

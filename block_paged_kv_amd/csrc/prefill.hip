@@ -54,6 +54,15 @@ struct PrefillParams {
   float scale_log2;
 };
 
+typedef short shortx4_t __attribute__((ext_vector_type(4)));
+
+// Transposing LDS read of four 16-bit values (see the P.V operand comment).
+__device__ __forceinline__ uint2 ds_read_tr16(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) shortx4_t lds_shortx4_t;
+  const shortx4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(p));
+  return __builtin_bit_cast(uint2, r);
+}
+
 __device__ __forceinline__ floatx4_t mfma16x16x32(const uint4& a, const uint4& b, floatx4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v, a),
                                                  __builtin_bit_cast(bf16x8v, b), c, 0, 0, 0);
@@ -61,15 +70,14 @@ __device__ __forceinline__ floatx4_t mfma16x16x32(const uint4& a, const uint4& b
 
 template <int D>
 __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillParams a) {
-  constexpr int KSTR = D + 8;        // K row stride in LDS (elements): spreads banks
-  constexpr int VSTR = kTileN + 8;   // V^T row stride in LDS (elements)
+  constexpr int KSTR = D + 8;        // K/V row stride in LDS (elements): spreads banks
   constexpr int DCH = D / 8;         // 16-byte chunks per key row
   constexpr int KS = D / 32;         // MFMA k-steps over head_dim
   constexpr int NT = D / 16;         // output column tiles
   constexpr float kNegInf = -INFINITY;
 
   __shared__ __attribute__((aligned(16))) uint16_t k_s[2][kTileN * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_s[2][D * VSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t v_s[2][kTileN * KSTR];
 
   // XCD-aware work mapping: XCD x takes work items [x*per_xcd, (x+1)*per_xcd).
   const int lin = blockIdx.x;
@@ -123,8 +131,11 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillParams a
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) o[j][nt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  float m[2] = {kNegInf, kNegInf};   // running max of raw scores
-  float l[2] = {0.f, 0.f};           // this lane's share of the running sum
+  float m[2] = {kNegInf, kNegInf};   // reference max of raw scores (per query row)
+  // Row sums accumulate on the matrix core: P times a ones tile gives, in the
+  // O layout, the sum of the same bf16 probabilities the numerator uses.
+  floatx4_t lsum[2] = {floatx4_t{0.f, 0.f, 0.f, 0.f}, floatx4_t{0.f, 0.f, 0.f, 0.f}};
+  const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
 
   const int32_t* bt = a.bt + static_cast<size_t>(b) * a.mb;
   const int bs_log2 = a.bs_log2;
@@ -141,92 +152,50 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillParams a
   };
   auto phys_ok = [&](int phys) { return phys > 0 && phys < a.nb; };
 
-  // Staging: wave w moves keys 16w .. 16w+15 of a tile (one block when
-  // block_size >= 16, so its base address is wave-uniform). K: lane l copies
-  // 16-byte chunk l % DCH of keys 16w + (64/DCH)*i + l / DCH. V: lane l owns
-  // the 4 keys 16w + 4*(l % 4) .. +3 and 16-byte chunk l / 4 (+16*i), which it
-  // writes transposed.
-  constexpr int KROWS = 64 / DCH;                 // keys one K load instruction covers
-  constexpr int KI = 16 / KROWS;                  // K loads per lane per tile
-  constexpr int VI = (DCH + 15) / 16;             // V units per lane per tile
-  uint4 kreg[KI];
-  uint4 vreg[VI][4];
+  // Staging (global -> registers -> LDS, double buffered): wave w moves keys
+  // 16w .. 16w+15 of a tile (one block when block_size >= 16, so its base
+  // address is wave-uniform); lane l copies 16-byte chunk l % DCH of keys
+  // 16w + (64/DCH)*i + l / DCH, for K and for V alike. Both stay row-major in
+  // LDS: the P.V operand is read with ds_read_b64_tr_b16, which hands each
+  // lane four consecutive keys of one head_dim column.
+  constexpr int KROWS = 64 / DCH;                 // keys one load instruction covers
+  constexpr int KI = 16 / KROWS;                  // loads per lane per tile (K, and V)
+  uint4 kreg[KI], vreg[KI];
   const int k_key = wave * 16 + lane / DCH;       // + KROWS * i
   const int k_dc = lane % DCH;
-  const int v_key = wave * 16 + 4 * (lane & 3);   // + e
-  const int v_dc = lane >> 2;                     // + 16 * i
-  // Physical block of key `key` of tile kt, from the tile's entries `ent`.
-  auto block_of = [&](int ent, int key) { return __shfl(ent, key >> bs_log2); };
-  auto row_ptr = [&](const uint16_t* pool, int phys, int kp) {
-    return pool + (((static_cast<size_t>(phys) * a.hkv + kvh) << bs_log2) + (kp & bs_mask)) * D;
-  };
+  // The wave's 16 keys lie in one block (block_size >= 16) or in two
+  // (block_size 8): their block ids come from the tile's entries by readlane,
+  // so block bases are wave-uniform.
   auto stage_load = [&](int kt, int ent) {
     const int ts = kt * kTileN;
+    const int e0 = (wave * 16) >> bs_log2;
+    const int phys_lo = __builtin_amdgcn_readlane(ent, e0);
+    const int phys_hi = __builtin_amdgcn_readlane(ent, bs_log2 == 3 ? e0 + 1 : e0);
     // Fast path: every key of the tile exists and every block id is valid.
-    const bool full = ts + kTileN <= n && __all(lane >= tile_blocks || phys_ok(ent));
-    if (full) {
+    const bool full = ts + kTileN <= n && phys_ok(phys_lo) && phys_ok(phys_hi);
+    const size_t base_lo = ((static_cast<size_t>(phys_lo) * a.hkv + kvh) << bs_log2) * D;
+    const size_t base_hi = ((static_cast<size_t>(phys_hi) * a.hkv + kvh) << bs_log2) * D;
 #pragma unroll
-      for (int i = 0; i < KI; ++i) {
-        const int key = k_key + KROWS * i;
-        kreg[i] = *reinterpret_cast<const uint4*>(row_ptr(a.k_pool, block_of(ent, key), ts + key) + k_dc * 8);
-      }
-#pragma unroll
-      for (int i = 0; i < VI; ++i) {
-        const int phys = block_of(ent, v_key);
-        if (v_dc + 16 * i < DCH) {  // always true unless head_dim == 64
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            vreg[i][e] = *reinterpret_cast<const uint4*>(row_ptr(a.v_pool, phys, ts + v_key + e) +
-                                                        (v_dc + 16 * i) * 8);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < KI; ++i) {
-        const int key = k_key + KROWS * i;
-        const int phys = block_of(ent, key);
+    for (int i = 0; i < KI; ++i) {
+      const int key = k_key + KROWS * i;                 // key within the tile
+      const bool hi = bs_log2 == 3 && ((key & 8) != 0);
+      const int phys = hi ? phys_hi : phys_lo;
+      const size_t off = (hi ? base_hi : base_lo) + static_cast<size_t>((ts + key) & bs_mask) * D + k_dc * 8;
+      if (full || (ts + key < n && phys_ok(phys))) {
+        kreg[i] = *reinterpret_cast<const uint4*>(a.k_pool + off);
+        vreg[i] = *reinterpret_cast<const uint4*>(a.v_pool + off);
+      } else {
         kreg[i] = make_uint4(0, 0, 0, 0);
-        if (ts + key < n && phys_ok(phys))
-          kreg[i] = *reinterpret_cast<const uint4*>(row_ptr(a.k_pool, phys, ts + key) + k_dc * 8);
-      }
-#pragma unroll
-      for (int i = 0; i < VI; ++i) {
-        const int phys = block_of(ent, v_key);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          vreg[i][e] = make_uint4(0, 0, 0, 0);
-          if (v_dc + 16 * i < DCH && ts + v_key + e < n && phys_ok(phys))
-            vreg[i][e] = *reinterpret_cast<const uint4*>(row_ptr(a.v_pool, phys, ts + v_key + e) +
-                                                        (v_dc + 16 * i) * 8);
-        }
+        vreg[i] = make_uint4(0, 0, 0, 0);
       }
     }
   };
-  // Registers -> LDS buffer `buf`: K row-major, V transposed.
   auto stage_store = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < KI; ++i)
-      *reinterpret_cast<uint4*>(&k_s[buf][(k_key + KROWS * i) * KSTR + k_dc * 8]) = kreg[i];
-#pragma unroll
-    for (int i = 0; i < VI; ++i) {
-      const int dc = v_dc + 16 * i;
-      if (dc < DCH) {
-        const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vreg[i][0]);
-        const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vreg[i][1]);
-        const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vreg[i][2]);
-        const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vreg[i][3]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // element 2e: low halves of the 4 keys; element 2e+1: high halves
-          uint2 lo2, hi2;
-          lo2.x = __builtin_amdgcn_perm(w1[e], w0[e], 0x05040100u);
-          lo2.y = __builtin_amdgcn_perm(w3[e], w2[e], 0x05040100u);
-          hi2.x = __builtin_amdgcn_perm(w1[e], w0[e], 0x07060302u);
-          hi2.y = __builtin_amdgcn_perm(w3[e], w2[e], 0x07060302u);
-          *reinterpret_cast<uint2*>(&vt_s[buf][(dc * 8 + 2 * e) * VSTR + v_key]) = lo2;
-          *reinterpret_cast<uint2*>(&vt_s[buf][(dc * 8 + 2 * e + 1) * VSTR + v_key]) = hi2;
-        }
-      }
+    for (int i = 0; i < KI; ++i) {
+      const int o = (k_key + KROWS * i) * KSTR + k_dc * 8;
+      *reinterpret_cast<uint4*>(&k_s[buf][o]) = kreg[i];
+      *reinterpret_cast<uint4*>(&v_s[buf][o]) = vreg[i];
     }
   };
 
@@ -244,7 +213,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillParams a
     }
     const int ts = kt * kTileN;
     const uint16_t* ks_buf = k_s[buf];
-    const uint16_t* vs_buf = vt_s[buf];
+    const uint16_t* vs_buf = v_s[buf];
 
     // ---- S^T = K Q^T : 4 key sub-tiles x 2 query tiles ----------------------
     floatx4_t s[2][4];
@@ -294,16 +263,11 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillParams a
         m[j] = mnew;
       }
       const float neg = m[j] == kNegInf ? 0.f : -m[j] * c;
-      float ls = 0.f;
       float pr[4][4];
 #pragma unroll
       for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pr[t4][i] = fast_exp2(fmaf(s[j][t4][i], c, neg));
-          ls += pr[t4][i];
-        }
-      l[j] = l[j] * alpha + ls;
+        for (int i = 0; i < 4; ++i) pr[t4][i] = fast_exp2(fmaf(s[j][t4][i], c, neg));
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         pa[j][kk].x = pack_bf16x2(pr[2 * kk][0], pr[2 * kk][1]);
@@ -320,21 +284,31 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillParams a
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) o[j][nt][i] *= al[i];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lsum[j][i] *= al[i];
       }
     }
 
     // ---- O += P V -------------------------------------------------------------
+    // B operand of step kk for lane (lq, lg): keys 32kk + 4lg + 0..3 and
+    // 32kk + 16 + 4lg + 0..3 (the key set of this lane's P elements) at head_dim
+    // column 16nt + lq. ds_read_b64_tr_b16 gives lane j of a 16-lane group
+    // element j%4 of the rows addressed by lanes 4k + j/4 (k = 0..3): lane j
+    // addresses row key0 + j/4, columns 16nt + 4(j%4) .. +3.
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+    for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const uint16_t* vrow = &vs_buf[(nt * 16 + lq) * VSTR + kk * 32 + lg * 4];
-        const uint2 v0 = *reinterpret_cast<const uint2*>(vrow);
-        const uint2 v1 = *reinterpret_cast<const uint2*>(vrow + 16);
+      for (int j = 0; j < 2; ++j) lsum[j] = mfma16x16x32(pa[j][kk], ones, lsum[j]);
+      const uint16_t* vbase = &vs_buf[(kk * 32 + 4 * lg + (lq >> 2)) * KSTR + 4 * (lq & 3)];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const uint2 v0 = ds_read_tr16(vbase + nt * 16);
+        const uint2 v1 = ds_read_tr16(vbase + 16 * KSTR + nt * 16);
         const uint4 vb = make_uint4(v0.x, v0.y, v1.x, v1.y);
 #pragma unroll
         for (int j = 0; j < 2; ++j) o[j][nt] = mfma16x16x32(pa[j][kk], vb, o[j][nt]);
       }
+    }
 
     if (has_next) stage_store(buf ^ 1);
     __syncthreads();
@@ -343,15 +317,9 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillParams a
   // ---- normalise and store --------------------------------------------------
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    float lt = l[j];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
     float inv[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float li = __shfl(lt, 4 * lg + i);
-      inv[i] = li > 0.f ? 1.f / li : 0.f;
-    }
+    for (int i = 0; i < 4; ++i) inv[i] = lsum[j][i] > 0.f ? 1.f / lsum[j][i] : 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = r_first + wave * kRowsPerWave + 16 * j + 4 * lg + i;
