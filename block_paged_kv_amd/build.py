@@ -33,6 +33,9 @@ HIP_FLAGS = [
     "-Wall", "-Wno-unused-result",
     "-I", INCLUDE, "-I", CSRC,
 ]
+# Per-source additions. The prefill kernel takes finite inputs only: without
+# NaN semantics its row maxima need no operand canonicalisation.
+HIP_EXTRA = {"prefill.hip": ["-fno-honor-nans"]}
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-I", CSRC]
 
 
@@ -55,7 +58,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     objs = []
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD_DIR, src + ".o")
-        steps.append([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        steps.append([HIPCC, *HIP_FLAGS, *HIP_EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     cxx = shutil.which("g++") or "g++"
     for src in CXX_SOURCES:

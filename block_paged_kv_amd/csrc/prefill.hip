@@ -10,9 +10,9 @@
 //   * Query rows are (position, query head) pairs of one KV head, packed
 //     position-major, so the G query heads sharing a KV head share every K/V
 //     tile. A workgroup of 4 waves owns 128 rows; each wave owns 32.
-//   * K/V tiles of 64 keys (whole blocks) are staged in LDS: K row-major
-//     (key, head_dim), V transposed (head_dim, key) by a 4x8 register
-//     transpose so the P.V operand reads consecutive keys.
+//   * K/V tiles of 64 keys (whole blocks) are staged in LDS, both row-major
+//     (key, head_dim); the P.V operand is read with a transposing LDS read
+//     (ds_read_b64_tr_b16), which hands each lane consecutive keys.
 //   * S^T = K Q^T and O += P V run on v_mfma_f32_16x16x32_bf16 with fp32
 //     accumulators; the S^T accumulator layout (one query per lane, 4 keys per
 //     register group) is exactly the A-operand layout P needs, once converted
@@ -24,6 +24,7 @@
 //     then serves the head's K/V to all of its tiles.
 
 #include <cmath>
+#include <type_traits>
 
 #include "device.h"
 #include "runtime.h"
@@ -63,6 +64,18 @@ __device__ __forceinline__ uint2 ds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(uint2, r);
 }
 
+// Maximum over the four lanes l % 16 + 16k (k = 0..3) that hold one query
+// row's scores: v_permlane32_swap pairs lane l with l ^ 32 and
+// v_permlane16_swap pairs l with l ^ 16; each returns both halves of the pair.
+__device__ __forceinline__ float max_across_groups(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  x = fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+  const unsigned w = __float_as_uint(x);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+}
+
 __device__ __forceinline__ floatx4_t mfma16x16x32(const uint4& a, const uint4& b, floatx4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v, a),
                                                  __builtin_bit_cast(bf16x8v, b), c, 0, 0, 0);
@@ -70,14 +83,19 @@ __device__ __forceinline__ floatx4_t mfma16x16x32(const uint4& a, const uint4& b
 
 template <int D>
 __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillParams a) {
-  constexpr int KSTR = D + 8;        // K/V row stride in LDS (elements): spreads banks
+  // LDS row strides (elements): rows padded by 32 bytes. Measured on gfx950
+  // with the two read patterns below (K: 16 rows x 64 bytes per ds_read_b128;
+  // V: 16 rows x 32 bytes per ds_read_b64_tr_b16), a 32-byte pad is the
+  // fastest of the paddings from 0 to 128 bytes for both.
+  constexpr int KSTR = D + 16;
+  constexpr int VSTR = D + 16;
   constexpr int DCH = D / 8;         // 16-byte chunks per key row
   constexpr int KS = D / 32;         // MFMA k-steps over head_dim
   constexpr int NT = D / 16;         // output column tiles
   constexpr float kNegInf = -INFINITY;
 
   __shared__ __attribute__((aligned(16))) uint16_t k_s[2][kTileN * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t v_s[2][kTileN * KSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t v_s[2][kTileN * VSTR];
 
   // XCD-aware work mapping: XCD x takes work items [x*per_xcd, (x+1)*per_xcd).
   const int lin = blockIdx.x;
@@ -131,7 +149,10 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillParams a
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) o[j][nt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  float m[2] = {kNegInf, kNegInf};   // reference max of raw scores (per query row)
+  // Reference max per query row in scaled log2 units (scale > 0, so the max
+  // of the raw scores scales to it), and its negation for the exponent.
+  float mc[2] = {kNegInf, kNegInf};
+  float negc[2] = {0.f, 0.f};
   // Row sums accumulate on the matrix core: P times a ones tile gives, in the
   // O layout, the sum of the same bf16 probabilities the numerator uses.
   floatx4_t lsum[2] = {floatx4_t{0.f, 0.f, 0.f, 0.f}, floatx4_t{0.f, 0.f, 0.f, 0.f}};
@@ -153,68 +174,69 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillParams a
   auto phys_ok = [&](int phys) { return phys > 0 && phys < a.nb; };
 
   // Staging (global -> registers -> LDS, double buffered): wave w moves keys
-  // 16w .. 16w+15 of a tile (one block when block_size >= 16, so its base
-  // address is wave-uniform); lane l copies 16-byte chunk l % DCH of keys
+  // 16w .. 16w+15 of a tile; lane l copies 16-byte chunk l % DCH of keys
   // 16w + (64/DCH)*i + l / DCH, for K and for V alike. Both stay row-major in
   // LDS: the P.V operand is read with ds_read_b64_tr_b16, which hands each
   // lane four consecutive keys of one head_dim column.
+  // The wave's 16 keys lie in one block (block_size >= 16) or in two
+  // (block_size 8, keys 8..15 in the second): block ids come from the tile's
+  // entries by readlane, so block bases are wave-uniform and each lane adds a
+  // loop-invariant 32-bit offset.
   constexpr int KROWS = 64 / DCH;                 // keys one load instruction covers
   constexpr int KI = 16 / KROWS;                  // loads per lane per tile (K, and V)
   uint4 kreg[KI], vreg[KI];
   const int k_key = wave * 16 + lane / DCH;       // + KROWS * i
   const int k_dc = lane % DCH;
-  // The wave's 16 keys lie in one block (block_size >= 16) or in two
-  // (block_size 8): their block ids come from the tile's entries by readlane,
-  // so block bases are wave-uniform.
+  const bool bs8 = bs_log2 == 3;
+  uint32_t lane_off[KI];
+#pragma unroll
+  for (int i = 0; i < KI; ++i)
+    lane_off[i] = static_cast<uint32_t>(((lane / DCH + KROWS * i) & (bs8 ? 7 : 15)) * D + k_dc * 8);
   auto stage_load = [&](int kt, int ent) {
     const int ts = kt * kTileN;
     const int e0 = (wave * 16) >> bs_log2;
     const int phys_lo = __builtin_amdgcn_readlane(ent, e0);
-    const int phys_hi = __builtin_amdgcn_readlane(ent, bs_log2 == 3 ? e0 + 1 : e0);
-    // Fast path: every key of the tile exists and every block id is valid.
-    const bool full = ts + kTileN <= n && phys_ok(phys_lo) && phys_ok(phys_hi);
-    const size_t base_lo = ((static_cast<size_t>(phys_lo) * a.hkv + kvh) << bs_log2) * D;
-    const size_t base_hi = ((static_cast<size_t>(phys_hi) * a.hkv + kvh) << bs_log2) * D;
+    const int phys_hi = __builtin_amdgcn_readlane(ent, bs8 ? e0 + 1 : e0);
+    // Element offset of the wave's first key inside its block (0 unless block_size > 16).
+    const size_t sub = static_cast<size_t>((ts + wave * 16) & bs_mask) * D;
+    const size_t base_lo = ((static_cast<size_t>(phys_lo) * a.hkv + kvh) << bs_log2) * D + sub;
+    const size_t base_hi = ((static_cast<size_t>(phys_hi) * a.hkv + kvh) << bs_log2) * D + sub;
+    if (ts + kTileN <= n && phys_ok(phys_lo) && phys_ok(phys_hi)) {
+      // Every key of the tile exists and every block id is valid.
 #pragma unroll
-    for (int i = 0; i < KI; ++i) {
-      const int key = k_key + KROWS * i;                 // key within the tile
-      const bool hi = bs_log2 == 3 && ((key & 8) != 0);
-      const int phys = hi ? phys_hi : phys_lo;
-      const size_t off = (hi ? base_hi : base_lo) + static_cast<size_t>((ts + key) & bs_mask) * D + k_dc * 8;
-      if (full || (ts + key < n && phys_ok(phys))) {
-        kreg[i] = *reinterpret_cast<const uint4*>(a.k_pool + off);
-        vreg[i] = *reinterpret_cast<const uint4*>(a.v_pool + off);
-      } else {
-        kreg[i] = make_uint4(0, 0, 0, 0);
-        vreg[i] = make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < KI; ++i) {
+        const size_t base = (bs8 && KROWS * i >= 8) ? base_hi : base_lo;
+        kreg[i] = *reinterpret_cast<const uint4*>(a.k_pool + base + lane_off[i]);
+        vreg[i] = *reinterpret_cast<const uint4*>(a.v_pool + base + lane_off[i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < KI; ++i) {
+        const bool hi = bs8 && KROWS * i >= 8;
+        const int phys = hi ? phys_hi : phys_lo;
+        const size_t base = hi ? base_hi : base_lo;
+        if (ts + k_key + KROWS * i < n && phys_ok(phys)) {
+          kreg[i] = *reinterpret_cast<const uint4*>(a.k_pool + base + lane_off[i]);
+          vreg[i] = *reinterpret_cast<const uint4*>(a.v_pool + base + lane_off[i]);
+        } else {
+          kreg[i] = make_uint4(0, 0, 0, 0);
+          vreg[i] = make_uint4(0, 0, 0, 0);
+        }
       }
     }
   };
   auto stage_store = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
-      const int o = (k_key + KROWS * i) * KSTR + k_dc * 8;
-      *reinterpret_cast<uint4*>(&k_s[buf][o]) = kreg[i];
-      *reinterpret_cast<uint4*>(&v_s[buf][o]) = vreg[i];
+      const int key = k_key + KROWS * i;
+      *reinterpret_cast<uint4*>(&k_s[buf][key * KSTR + k_dc * 8]) = kreg[i];
+      *reinterpret_cast<uint4*>(&v_s[buf][key * VSTR + k_dc * 8]) = vreg[i];
     }
   };
 
-  int ent_next = load_entries(kt_begin + 1);
-  stage_load(kt_begin, load_entries(kt_begin));
-  stage_store(0);
-  __syncthreads();
-
-  for (int kt = kt_begin; kt <= kt_end; ++kt) {
-    const int buf = (kt - kt_begin) & 1;
-    const bool has_next = kt < kt_end;
-    if (has_next) {  // tile kt+1 streams into registers while tile kt computes
-      stage_load(kt + 1, ent_next);
-      ent_next = load_entries(kt + 2);
-    }
-    const int ts = kt * kTileN;
-    const uint16_t* ks_buf = k_s[buf];
-    const uint16_t* vs_buf = v_s[buf];
-
+  // One K/V tile: S^T = K Q^T, online softmax, O += P V. Instantiated twice:
+  // tiles that lie wholly inside every row's [lo, a] range skip the mask.
+  auto compute_tile = [&](bool need_mask, int ts, const uint16_t* ks_buf, const uint16_t* vs_buf) {
     // ---- S^T = K Q^T : 4 key sub-tiles x 2 query tiles ----------------------
     floatx4_t s[2][4];
 #pragma unroll
@@ -231,43 +253,48 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillParams a
       }
 
     // ---- online softmax (lane: query 16j+lq, keys ts + 16*t4 + 4*lg + i) ------
-    const bool need_mask = (ts + kTileN - 1 > a_min) || (ts < lo_max);
     uint4 pa[2][2];  // P as bf16 A operands: [query tile][32-key step]
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       if (need_mask) {
+        // Rows past the tile's last row keep their (zero-query) scores: their
+        // outputs are never stored. The empty asm makes the bounds opaque so
+        // the compares stay inside this rarely taken branch.
+        int lo_rel = qlo[j] - ts - 4 * lg;
+        int hi_rel = qpos[j] - ts - 4 * lg;
+        asm volatile("" : "+v"(lo_rel), "+v"(hi_rel));
 #pragma unroll
         for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int kp = ts + t4 * 16 + lg * 4 + i;
-            if (!(kp >= qlo[j] && kp <= qpos[j] && qvalid[j])) s[j][t4][i] = kNegInf;
+            const int e = t4 * 16 + i;
+            if (e < lo_rel || e > hi_rel) s[j][t4][i] = kNegInf;
           }
       }
-      float mx = kNegInf;
+      // Chained pairs so that each step is one v_max3_f32.
+      float mx = fmaxf(s[j][0][0], s[j][0][1]);
 #pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4)
-        mx = fmaxf(fmaxf(mx, fmaxf(s[j][t4][0], s[j][t4][1])), fmaxf(s[j][t4][2], s[j][t4][3]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      // Lazy rescaling: keep the reference max m[j] until a score exceeds it by
-      // more than 2^8 (in log2 units); until then probabilities stay <= 256,
+      for (int e = 2; e < 16; e += 2)
+        mx = fmaxf(fmaxf(mx, s[j][e >> 2][e & 3]), s[j][e >> 2][(e & 3) + 1]);
+      mx = max_across_groups(mx);
+      // Lazy rescaling: keep the reference max mc[j] until a score exceeds it
+      // by more than 2^8 (in log2 units); until then probabilities stay <= 256,
       // harmless in fp32 and bf16, and the final division by the sum taken
       // with the same reference cancels the choice exactly.
-      const bool grow = __any(mx * c > (m[j] == kNegInf ? kNegInf : m[j] * c) + 8.f);
+      const float mxc = mx * c;
+      const bool grow = __any(mxc > mc[j] + 8.f);
       float alpha = 1.f;
       if (grow) {
-        const float mnew = fmaxf(m[j], mx);
-        const float mref = mnew == kNegInf ? 0.f : mnew;
-        alpha = fast_exp2((m[j] - mref) * c);
-        m[j] = mnew;
+        const float mnew = fmaxf(mc[j], mxc);
+        alpha = mnew == kNegInf ? 1.f : fast_exp2(mc[j] - mnew);
+        mc[j] = mnew;
+        negc[j] = mnew == kNegInf ? 0.f : -mnew;
       }
-      const float neg = m[j] == kNegInf ? 0.f : -m[j] * c;
       float pr[4][4];
 #pragma unroll
       for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pr[t4][i] = fast_exp2(fmaf(s[j][t4][i], c, neg));
+        for (int i = 0; i < 4; ++i) pr[t4][i] = fast_exp2(fmaf(s[j][t4][i], c, negc[j]));
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         pa[j][kk].x = pack_bf16x2(pr[2 * kk][0], pr[2 * kk][1]);
@@ -299,17 +326,34 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillParams a
     for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) lsum[j] = mfma16x16x32(pa[j][kk], ones, lsum[j]);
-      const uint16_t* vbase = &vs_buf[(kk * 32 + 4 * lg + (lq >> 2)) * KSTR + 4 * (lq & 3)];
+      const uint16_t* vbase = &vs_buf[(kk * 32 + 4 * lg + (lq >> 2)) * VSTR + 4 * (lq & 3)];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const uint2 v0 = ds_read_tr16(vbase + nt * 16);
-        const uint2 v1 = ds_read_tr16(vbase + 16 * KSTR + nt * 16);
+        const uint2 v1 = ds_read_tr16(vbase + 16 * VSTR + nt * 16);
         const uint4 vb = make_uint4(v0.x, v0.y, v1.x, v1.y);
 #pragma unroll
         for (int j = 0; j < 2; ++j) o[j][nt] = mfma16x16x32(pa[j][kk], vb, o[j][nt]);
       }
     }
+  };
 
+  int ent_next = load_entries(kt_begin + 1);
+  stage_load(kt_begin, load_entries(kt_begin));
+  stage_store(0);
+  __syncthreads();
+
+  for (int kt = kt_begin; kt <= kt_end; ++kt) {
+    const int buf = (kt - kt_begin) & 1;
+    const bool has_next = kt < kt_end;
+    if (has_next) {  // tile kt+1 streams into registers while tile kt computes
+      stage_load(kt + 1, ent_next);
+      ent_next = load_entries(kt + 2);
+    }
+    const int ts = kt * kTileN;
+    // A tile needs the mask when it reaches past the first row's position or
+    // starts before the last row's window start.
+    compute_tile((ts + kTileN - 1 > a_min) || (ts < lo_max), ts, k_s[buf], v_s[buf]);
     if (has_next) stage_store(buf ^ 1);
     __syncthreads();
   }
@@ -358,7 +402,8 @@ extern "C" int32_t paged_attn_prefill_chunk(void* out, const void* q, const void
   if (batch < 0 || total_q < 0 || max_q_len < 0 || max_blocks_per_seq < 1 || num_blocks < 1 ||
       sliding_window < 0)
     return fail(PAGED_ERR_INVALID_ARG, "bad size argument");
-  if (!std::isfinite(scale)) return fail(PAGED_ERR_INVALID_ARG, "scale must be finite");
+  if (!std::isfinite(scale) || scale < 0.f)
+    return fail(PAGED_ERR_INVALID_ARG, "scale must be finite and non-negative");
   if (batch == 0 || total_q == 0 || max_q_len == 0) return ok();
   if (!out || !q || !k_pool || !v_pool || !block_tables || !cu_q_lens || !seq_lens)
     return fail(PAGED_ERR_INVALID_ARG, "NULL pointer");

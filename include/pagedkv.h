@@ -171,7 +171,9 @@ int32_t paged_attn_decode(void* out, const void* q, const void* k_pool, const vo
  * Query i of the chunk sits at position a = P + i and attends to keys
  * [lo, a], lo = max(0, a - sliding_window + 1) when sliding_window > 0 else 0
  * (causal inside the chunk). bf16 only; the products run on MFMA with float32
- * accumulation, probabilities rounded to bf16 for the P.V product.
+ * accumulation, probabilities rounded to bf16 for the P.V product. scale must
+ * be finite and >= 0 (PAGED_ERR_INVALID_ARG otherwise); q, K and V must be
+ * finite (NaN inputs give unspecified results).
  *   out, q       : device bf16, [total_q][num_q_heads][head_dim]
  *   cu_q_lens    : device int32 [batch + 1], cu_q_lens[0] = 0, nondecreasing,
  *                  cu_q_lens[batch] = total_q, each chunk <= max_q_len

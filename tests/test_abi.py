@@ -79,6 +79,11 @@ def test_prefill_argument_errors():
     rc = L.paged_attn_prefill_chunk(None, None, None, None, None, 4, None, None, 1, 0, 8, 8, 8, 128,
                                     16, 8, 0.1, 0, pk.PAGED_BF16, None)
     assert rc == pk.PAGED_OK
+    # negative or non-finite scale
+    for bad in (-0.1, float("nan")):
+        rc = L.paged_attn_prefill_chunk(None, None, None, None, None, 4, None, None, 1, 8, 8, 8, 8, 128,
+                                        16, 8, bad, 0, pk.PAGED_BF16, None)
+        assert rc == pk.PAGED_ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("B,hq,hkv,d,msl,w,part", [
