@@ -238,6 +238,10 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillParams a
   // tiles that lie wholly inside every row's [lo, a] range skip the mask.
   auto compute_tile = [&](bool need_mask, int ts, const uint16_t* ks_buf, const uint16_t* vs_buf) {
     // ---- S^T = K Q^T : 4 key sub-tiles x 2 query tiles ----------------------
+    // The S^T burst runs at raised wave priority: while one wave issues its
+    // back-to-back MFMAs, the other wave on the SIMD fills the gaps with its
+    // softmax work (measured: about 4% faster than equal priority).
+    __builtin_amdgcn_s_setprio(1);
     floatx4_t s[2][4];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -253,13 +257,13 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillParams a
       }
 
     // ---- online softmax (lane: query 16j+lq, keys ts + 16*t4 + 4*lg + i) ------
-    uint4 pa[2][2];  // P as bf16 A operands: [query tile][32-key step]
+    __builtin_amdgcn_s_setprio(0);
+    if (need_mask) {
+      // Rows past the tile's last row keep their (zero-query) scores: their
+      // outputs are never stored. The empty asm makes the bounds opaque so
+      // the compares stay inside this rarely taken branch.
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      if (need_mask) {
-        // Rows past the tile's last row keep their (zero-query) scores: their
-        // outputs are never stored. The empty asm makes the bounds opaque so
-        // the compares stay inside this rarely taken branch.
+      for (int j = 0; j < 2; ++j) {
         int lo_rel = qlo[j] - ts - 4 * lg;
         int hi_rel = qpos[j] - ts - 4 * lg;
         asm volatile("" : "+v"(lo_rel), "+v"(hi_rel));
@@ -271,25 +275,44 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillParams a
             if (e < lo_rel || e > hi_rel) s[j][t4][i] = kNegInf;
           }
       }
-      // Chained pairs so that each step is one v_max3_f32.
+    }
+    // Row maxima in scaled log2 units; chained pairs so each step is one v_max3_f32.
+    float mxc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
       float mx = fmaxf(s[j][0][0], s[j][0][1]);
 #pragma unroll
       for (int e = 2; e < 16; e += 2)
         mx = fmaxf(fmaxf(mx, s[j][e >> 2][e & 3]), s[j][e >> 2][(e & 3) + 1]);
-      mx = max_across_groups(mx);
-      // Lazy rescaling: keep the reference max mc[j] until a score exceeds it
-      // by more than 2^8 (in log2 units); until then probabilities stay <= 256,
-      // harmless in fp32 and bf16, and the final division by the sum taken
-      // with the same reference cancels the choice exactly.
-      const float mxc = mx * c;
-      const bool grow = __any(mxc > mc[j] + 8.f);
-      float alpha = 1.f;
-      if (grow) {
-        const float mnew = fmaxf(mc[j], mxc);
-        alpha = mnew == kNegInf ? 1.f : fast_exp2(mc[j] - mnew);
+      mxc[j] = max_across_groups(mx) * c;
+    }
+    // Lazy rescaling: keep the reference max mc[j] until a score exceeds it by
+    // more than 2^8 (in log2 units); until then probabilities stay <= 256,
+    // harmless in fp32 and bf16, and the final division by the sum taken with
+    // the same reference cancels the choice exactly. One vote covers both
+    // query tiles, so the common path has no branch between the two.
+    if (__any(mxc[0] > mc[0] + 8.f || mxc[1] > mc[1] + 8.f)) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float mnew = fmaxf(mc[j], mxc[j]);
+        const float alpha = mnew == kNegInf ? 1.f : fast_exp2(mc[j] - mnew);
         mc[j] = mnew;
         negc[j] = mnew == kNegInf ? 0.f : -mnew;
+        // Rescale O rows (O layout: lane holds queries 16j + 4*lg + i).
+        float al[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * lg + i);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[j][nt][i] *= al[i];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lsum[j][i] *= al[i];
       }
+    }
+    uint4 pa[2][2];  // P as bf16 A operands: [query tile][32-key step]
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
       float pr[4][4];
 #pragma unroll
       for (int t4 = 0; t4 < 4; ++t4)
@@ -301,18 +324,6 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillParams a
         pa[j][kk].y = pack_bf16x2(pr[2 * kk][2], pr[2 * kk][3]);
         pa[j][kk].z = pack_bf16x2(pr[2 * kk + 1][0], pr[2 * kk + 1][1]);
         pa[j][kk].w = pack_bf16x2(pr[2 * kk + 1][2], pr[2 * kk + 1][3]);
-      }
-      // Rescale O rows (O layout: lane holds queries 16j + 4*lg + i).
-      if (grow) {
-        float al[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * lg + i);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) o[j][nt][i] *= al[i];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) lsum[j][i] *= al[i];
       }
     }
 
