@@ -58,7 +58,7 @@ struct DecodeParams {
   const void* v_pool;
   const int32_t* bt;
   const int32_t* seq_lens;
-  int32_t batch, mb, hq, hkv, group, head_groups, bs_log2, nb, window, part, max_parts;
+  int32_t batch, mb, hq, hkv, group, gt, head_groups, bs_log2, nb, window, part, max_parts;
   float scale_log2;  // scale * log2(e)
 };
 
@@ -336,66 +336,102 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodePa
 }
 
 // ---------------------------------------------------------------------------
-// bf16 decode with q.K on the matrix cores.
+// bf16 decode: K/V streamed into LDS by the load unit, both products on MFMA.
 //
-// Per 16-token K tile, S = Q K^T is one v_mfma_f32_16x16x32_bf16 per 32
-// head_dim elements: the A operand holds the (up to 8) query heads of the
-// group as rows (zero-padded to 16), the B operand the tile's 16 keys. K is
-// loaded in exactly that operand layout -- lane l reads 16 bytes of token
-// l%16 -- so the token a lane loads is also the score column it receives, and
-// validity masks need no shuffle. Lane l then holds the scores of heads
-// 4*(l/16)+i, i < 4, for token l%16 of each tile: the row max is a 16-lane DPP
-// reduction, and probabilities go through a small per-wave LDS buffer to the
-// P.V layout. P.V stays on VALU: V is read 16 bytes per lane with R = D/8 lanes
-// per token row (coalesced; each lane owns 8 head_dim elements, so the fp32
-// accumulators take GT*8 registers), and two tokens at a time are combined by
-// v_dot2_f32_bf16 on bf16 (p_a, p_b) and (v_a, v_b) pairs built with v_perm.
-// Probabilities are rounded to bf16 for that product only; max, sum and the
-// accumulators stay fp32.
-template <int D, int GT>
-struct MfmaGeo {
-  static constexpr int KS = D / 32;                        // MFMA k-steps per K tile
-  static constexpr int KT = D == 64 ? 8 : D == 128 ? 4 : 2;  // K tiles per iteration
-  static constexpr int NTOK = 16 * KT;                     // tokens per wave iteration
-  static constexpr int R = D / 8;                          // V: lanes per token row (8..32)
-  static constexpr int CPL = (D / 8) / R;                  // V: 16-byte chunks per lane per token
-  static constexpr int TPW = 64 / R;                       // V: token rows per wave load
-  static constexpr int U = NTOK / TPW;                     // V: token groups per iteration (even)
-  static constexpr int EPL = CPL * 8;                      // V: head_dim elements per lane
-  static constexpr int GTP = GT <= 4 ? 4 : 8;              // heads per token in the p buffer
+// Each wave of a workgroup owns a contiguous run of 16-token stages of the
+// partition and a private ring of two stage buffers in LDS. A stage's K and V
+// rows (16 tokens x head_dim, row-major) are fetched with
+// global_load_lds_dwordx4: every lane names its own 16-byte source and the
+// data lands at the ring slot's base + 16 * lane, with no registers held and
+// no barrier (only the wave itself reads its ring). One stage streams in
+// while the other is being computed.
+//   * S^T (16 keys x 16 heads) = K Q^T on v_mfma_f32_16x16x32_bf16: the A
+//     operand is read from the K rows, the B operand is the query heads of
+//     the group (zero beyond GT), held in registers for the whole partition.
+//     Lane (lq, lg) receives the scores of head lq for keys 4*lg + i.
+//   * O (16 heads x head_dim) += P V on v_mfma_f32_16x16x16_bf16: the S^T
+//     accumulator layout is exactly the P operand layout (head lq, keys
+//     4*lg .. 4*lg + 3), and the V operand (4 consecutive keys of one head_dim
+//     column) comes from the row-major V rows through ds_read_b64_tr_b16.
+//     Row sums come from the same product against a ones tile.
+//   * Rows are stored in LDS with the 16-byte chunk index XOR-ed by the row
+//     index, which spreads the column reads of both products over the banks.
+//   * Online softmax in scaled log2 units with lazy rescaling (the reference
+//     max moves only when a score exceeds it by 2^8); the partition's
+//     (max, sum, accumulator) are exact for whatever reference is kept.
+template <int D>
+struct StageGeo {
+  static constexpr int ROWB = D * 2;            // bytes per token row
+  static constexpr int CPT = D / 8;             // 16-byte chunks per token row
+  static constexpr int TPI = 1024 / ROWB;       // token rows per load instruction (1 KiB)
+  static constexpr int NI = 16 / TPI;           // load instructions per stage, K (and V)
+  static constexpr int SBYTES = 16 * ROWB;      // K (or V) bytes of one stage
+  static constexpr int KS = D / 32;             // q.K k-steps
+  static constexpr int NT = D / 16;             // output column tiles
+  static constexpr int SWZ = CPT < 16 ? CPT - 1 : 15;  // row bits folded into the chunk index
 };
 
-template <int R>
-__device__ __forceinline__ float group_max(float x) {
-  if constexpr (R >= 2) x = fmaxf(x, dpp_mov<0xB1>(x));
-  if constexpr (R >= 4) x = fmaxf(x, dpp_mov<0x4E>(x));
-  if constexpr (R >= 8) x = fmaxf(x, dpp_mov<0x141>(x));
-  if constexpr (R >= 16) x = fmaxf(x, dpp_mov<0x140>(x));
-  return x;
+constexpr int kStageTokens = 16;
+constexpr int kDecodeWaves = 4;
+
+typedef short shortx4d_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8d_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ floatx4_t mfma_k32(const uint4& a, const uint4& b, floatx4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8d_t, a),
+                                                 __builtin_bit_cast(bf16x8d_t, b), c, 0, 0, 0);
 }
 
-typedef __bf16 bf16x8v_t __attribute__((ext_vector_type(8)));
-
-__device__ __forceinline__ floatx4_t mfma_16x16x32(const uint4& a, const uint4& b, floatx4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v_t, a),
-                                                 __builtin_bit_cast(bf16x8v_t, b), c, 0, 0, 0);
+__device__ __forceinline__ floatx4_t mfma_k16(const uint2& a, const uint2& b, floatx4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(shortx4d_t, a),
+                                                   __builtin_bit_cast(shortx4d_t, b), c, 0, 0, 0);
 }
 
-template <int D, int GT>
-__global__ __launch_bounds__(64 * kMaxWaves, 2) void decode_partial_mfma_kernel(DecodeParams a) {
-  using Gm = MfmaGeo<D, GT>;
-  constexpr int KS = Gm::KS, KT = Gm::KT, NTOK = Gm::NTOK, R = Gm::R, CPL = Gm::CPL;
-  constexpr int TPW = Gm::TPW, U = Gm::U, EPL = Gm::EPL, GTP = Gm::GTP;
+// 16 zero bytes in the code object: the load source of token rows a stage
+// does not attend, so those LDS rows hold finite zeros.
+__device__ __attribute__((aligned(16))) const uint4 kZeroChunk = {0u, 0u, 0u, 0u};
+
+// global_load_lds_dwordx4: each lane copies 16 bytes from its own global
+// address to lds_dst + 16 * lane. Issued as assembly so that the compiler
+// leaves the vector-memory counter to the stage pipeline below (it would
+// otherwise drain every outstanding load before each LDS read). M0 holds the
+// destination; nothing else in these kernels uses M0.
+__device__ __forceinline__ void lds_dma16(const void* gaddr, const void* lds_dst) {
+  const uint32_t dst = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)(lds_dst))));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(dst), "v"(gaddr) : "memory");
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+// One stage buffer: K rows then V rows.
+template <int D>
+struct StageBuf {
+  uint4 k[StageGeo<D>::SBYTES / 16];
+  uint4 v[StageGeo<D>::SBYTES / 16];
+};
+
+template <int D>
+__global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_lds_kernel(DecodeParams a) {
+  using Sg = StageGeo<D>;
+  constexpr int CPT = Sg::CPT, TPI = Sg::TPI, NI = Sg::NI, KS = Sg::KS, NT = Sg::NT;
+  constexpr int ROWB = Sg::ROWB, SWZ = Sg::SWZ;
   constexpr float kNegInf = -INFINITY;
 
-  __shared__ float sm_acc[kMaxWaves][GT][D];
-  __shared__ float sm_m[kMaxWaves][GT];
-  __shared__ float sm_l[kMaxWaves][GT];
-  __shared__ __attribute__((aligned(16))) float sm_p[kMaxWaves][NTOK * GTP];
+  // One ring slot per array, so the compiler can tell the slots apart when it
+  // orders LDS reads against the loads still writing other slots.
+  __shared__ StageBuf<D> ring0[kDecodeWaves];
+  __shared__ StageBuf<D> ring1[kDecodeWaves];
 
   const int p = blockIdx.x;
   const int hg = blockIdx.y;
   const int b = blockIdx.z;
+  const int GT = a.gt;
   const int kvh = hg / a.head_groups;
   const int h0 = kvh * a.group + (hg - kvh * a.head_groups) * GT;
   const int n = a.seq_lens[b];
@@ -405,6 +441,8 @@ __global__ __launch_bounds__(64 * kMaxWaves, 2) void decode_partial_mfma_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6;
+  const int lq = lane & 15;
+  const int lg = lane >> 4;
 
   if (ps >= n) {
     // Only an empty row (n == 0) reaches this with p == 0: its output is zero.
@@ -415,189 +453,215 @@ __global__ __launch_bounds__(64 * kMaxWaves, 2) void decode_partial_mfma_kernel(
   }
   const int t_begin = max(ps, lo);
   const int t_end = min(ps + a.part, n);
-  const int lq = lane & 15;  // K: token within a tile; S: score column
-  const int lg = lane >> 4;  // K: 16-byte chunk group; S: head group (heads 4*lg + i)
-  const int sub = lane % R;  // V: chunk within the token row
-  const int tl = lane / R;   // V: token within a group
   const int bs_log2 = a.bs_log2;
   const int bs_mask = (1 << bs_log2) - 1;
+  const bool bs8 = bs_log2 == 3;
 
-  // A operand: head row lq (zero beyond GT), elements 8*(lg + 4j) .. +8 of step j.
-  uint4 qa[KS];
+  // This wave's stages: a contiguous share of the partition's 16-token
+  // stages, clipped to those that touch [t_begin, t_end).
+  const int nst_part = a.part / kStageTokens;
+  const int spw = (nst_part + nw - 1) / nw;
+  const int k_first = max(wave * spw, (t_begin - ps) / kStageTokens);
+  const int k_last = min(min((wave + 1) * spw, nst_part), (t_end - ps + kStageTokens - 1) / kStageTokens);
+  const int nst = max(0, k_last - k_first);  // stages this wave computes
+  const int ts0 = ps + k_first * kStageTokens;
+
+  // Query heads h0 .. h0+GT-1 as the B operand of S^T = K Q^T: lane (lq, lg)
+  // holds head lq, head_dim elements 32*ks + 8*lg .. +8.
+  uint4 qb[KS];
   {
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
                            (static_cast<size_t>(b) * a.hq + h0 + (lq < GT ? lq : 0)) * D;
 #pragma unroll
-    for (int j = 0; j < KS; ++j)
-      qa[j] = lq < GT ? *reinterpret_cast<const uint4*>(qrow + 8 * (lg + 4 * j)) : make_uint4(0, 0, 0, 0);
+    for (int ks = 0; ks < KS; ++ks)
+      qb[ks] = lq < GT ? *reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * lg) : make_uint4(0, 0, 0, 0);
   }
 
-  float mrun[4], lrun[4];  // S layout: heads 4*lg + i
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    mrun[i] = kNegInf;
-    lrun[i] = 0.f;
-  }
-  float acc[GT][EPL];      // V layout: head_dim elements (j*R + sub)*8 + e
-#pragma unroll
-  for (int g = 0; g < GT; ++g)
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
-
+  // Block-table window: lane i holds the entry of block tb0 + i.
   const int32_t* bt = a.bt + static_cast<size_t>(b) * a.mb;
-  const char* kpool = static_cast<const char*>(a.k_pool);
-  const char* vpool = static_cast<const char*>(a.v_pool);
-  const float c = a.scale_log2;
-  float* pbuf = sm_p[wave];
+  const int blk_end = nst > 0 ? ((ts0 + nst * kStageTokens - 1) >> bs_log2) + 1 : 0;
+  int tb0 = 0;
+  int tbl = 0;
+  auto phys_ok = [&](int phys) { return phys > 0 && phys < a.nb; };
 
-  // Table entries of one iteration (lane l: l-th block), prefetched one ahead.
-  const int it_blocks = NTOK > (1 << bs_log2) ? (NTOK >> bs_log2) : 1;
-  auto load_table = [&](int it) -> int {
-    const int lb = (it >> bs_log2) + lane;
-    return (it < t_end && lane < it_blocks && lb < a.mb && (lb << bs_log2) < t_end) ? bt[lb] : 0;
+  // Lane offsets (elements) inside a block for each load instruction: the
+  // instruction's token row i*TPI + lane/CPT, global chunk (lane%CPT) ^ row.
+  uint32_t lane_off[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int row = i * TPI + lane / CPT;
+    const int chunk = (lane % CPT) ^ (row & SWZ);
+    lane_off[i] = static_cast<uint32_t>((row & (bs8 ? 7 : 15)) * D + chunk * 8);
+  }
+  const uint16_t* kpool = static_cast<const uint16_t*>(a.k_pool);
+  const uint16_t* vpool = static_cast<const uint16_t*>(a.v_pool);
+
+  // Issue the loads of stage k (0-based within this wave) into ring slot sb:
+  // exactly 2*NI load instructions, every lane active (rows the stage does
+  // not attend read the zero chunk). Returns the stage's valid-token mask
+  // (bit t: token ts + t is attended and its block id is valid). The block
+  // ids come from the table window, loaded before any stage is in flight.
+  auto issue = [&](int k, StageBuf<D>* sb) -> uint32_t {
+    const int ts = ts0 + k * kStageTokens;
+    const int blk = ts >> bs_log2;
+    const int phys_lo = __builtin_amdgcn_readlane(tbl, blk - tb0);
+    const int phys_hi = __builtin_amdgcn_readlane(tbl, bs8 ? blk + 1 - tb0 : blk - tb0);
+    const size_t sub = static_cast<size_t>(ts & bs_mask) * D;
+    const size_t base_lo = ((static_cast<size_t>(phys_lo) * a.hkv + kvh) << bs_log2) * D + sub;
+    const size_t base_hi = ((static_cast<size_t>(phys_hi) * a.hkv + kvh) << bs_log2) * D + sub;
+    const int v0 = min(max(t_begin - ts, 0), kStageTokens);
+    const int v1 = min(max(t_end - ts, 0), kStageTokens);
+    uint32_t vmask = v1 > v0 ? ((0xFFFFu >> (kStageTokens - v1)) & ~((1u << v0) - 1u)) : 0u;
+    if (!phys_ok(phys_lo)) vmask &= bs8 ? 0xFF00u : 0u;
+    if (!phys_ok(phys_hi)) vmask &= bs8 ? 0x00FFu : 0u;
+    // The slot's previous stage has been consumed; its LDS reads must have
+    // returned before the new data lands.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const size_t base = (bs8 && i * TPI >= 8) ? base_hi : base_lo;
+      const bool ok = (vmask >> (i * TPI + lane / CPT)) & 1u;
+      const void* ksrc = ok ? static_cast<const void*>(kpool + base + lane_off[i]) : &kZeroChunk;
+      const void* vsrc = ok ? static_cast<const void*>(vpool + base + lane_off[i]) : &kZeroChunk;
+      lds_dma16(ksrc, &sb->k[i * 64]);
+      lds_dma16(vsrc, &sb->v[i * 64]);
+    }
+    return vmask;
   };
-  int tbl = load_table(ps + wave * NTOK);
 
-  for (int it = ps + wave * NTOK; it < t_end; it += nw * NTOK) {
-    const int blk0 = it >> bs_log2;
-    uint4 kb[KT][KS];
-    bool kval[KT];
+  floatx4_t o[NT];
 #pragma unroll
-    for (int t = 0; t < KT; ++t) {
-      const int tok = it + 16 * t + lq;
-      const int phys = __shfl(tbl, (tok >> bs_log2) - blk0);
-      kval[t] = tok >= t_begin && tok < t_end && phys > 0 && phys < a.nb;
-      const char* src = kpool + ((((static_cast<size_t>(phys) * a.hkv + kvh) << bs_log2) + (tok & bs_mask)) * D +
-                                 8 * lg) * 2;
-      if (kval[t]) {
-#pragma unroll
-        for (int j = 0; j < KS; ++j) kb[t][j] = *reinterpret_cast<const uint4*>(src + 64 * j);
-      } else {
-#pragma unroll
-        for (int j = 0; j < KS; ++j) kb[t][j] = make_uint4(0, 0, 0, 0);
-      }
-    }
-    uint4 vr[U][CPL];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int tg = it + TPW * u;
-      const int phys = __builtin_amdgcn_readlane(tbl, (tg >> bs_log2) - blk0);
-      const int tok = tg + tl;
-      const bool ok = tok >= t_begin && tok < t_end && phys > 0 && phys < a.nb;
-      const char* src = vpool + ((((static_cast<size_t>(phys) * a.hkv + kvh) << bs_log2) + (tok & bs_mask)) * D) * 2 +
-                        16 * sub;
-      if (ok) {
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) vr[u][j] = *reinterpret_cast<const uint4*>(src + 16 * R * j);
-      } else {
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) vr[u][j] = make_uint4(0, 0, 0, 0);
-      }
-    }
-    tbl = load_table(it + nw * NTOK);
+  for (int nt = 0; nt < NT; ++nt) o[nt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  floatx4_t lsum = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  float mc = kNegInf;    // reference max of head lq (scaled log2 units)
+  float negc = 0.f;
+  const uint2 ones = make_uint2(0x3F803F80u, 0x3F803F80u);
+  const float c = a.scale_log2;
 
-    // ---- scores on MFMA: lane holds S[4*lg + i][16t + lq] ---------------------
-    floatx4_t sacc[KT];
+  auto compute = [&](const StageBuf<D>* sb, uint32_t vmask) {
+    // ---- S^T = K Q^T --------------------------------------------------------
+    floatx4_t s = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < KT; ++t) {
-      sacc[t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < KS; ++j) sacc[t] = mfma_16x16x32(qa[j], kb[t][j], sacc[t]);
+    for (int ks = 0; ks < KS; ++ks) {
+      const int chunk = (4 * ks + lg) ^ (lq & SWZ);
+      const uint4 ka = *reinterpret_cast<const uint4*>(
+          reinterpret_cast<const char*>(sb->k) + lq * ROWB + chunk * 16);
+      s = mfma_k32(ka, qb[ks], s);
     }
+    // ---- mask (stages that straddle the range or hold an invalid block) ------
+    if (vmask != 0xFFFFu) {
+      // The empty asm keeps the per-key tests inside this rarely taken branch.
+      uint32_t bits = vmask >> (4 * lg);
+      asm volatile("" : "+v"(bits));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (!((bits >> i) & 1u)) s[i] = kNegInf;
+    }
+    // ---- online softmax (lane: head lq, keys ts + 4*lg + i) -----------------
+    const float mxc = max_across_groups(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]))) * c;
+    if (__any(mxc > mc + 8.f)) {
+      const float mnew = fmaxf(mc, mxc);
+      const float alpha = mnew == kNegInf ? 1.f : fast_exp2(mc - mnew);
+      mc = mnew;
+      negc = mnew == kNegInf ? 0.f : -mnew;
+      float al[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * lg + i);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[nt][i] *= al[i];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lsum[i] *= al[i];
+    }
+    uint2 pa;
+    pa.x = pack_bf16x2(fast_exp2(fmaf(s[0], c, negc)), fast_exp2(fmaf(s[1], c, negc)));
+    pa.y = pack_bf16x2(fast_exp2(fmaf(s[2], c, negc)), fast_exp2(fmaf(s[3], c, negc)));
+    // ---- O += P V ---------------------------------------------------------------
+    // Lane (lq, lg) addresses key row 4*lg + lq/4, columns 16*nt + 4*(lq%4) .. +3;
+    // the transposing read returns keys 4*lg .. 4*lg+3 of column 16*nt + lq.
+    const int vrow = 4 * lg + (lq >> 2);
+    const char* vr = reinterpret_cast<const char*>(sb->v) + vrow * ROWB + 8 * (lq & 1);
+    lsum = mfma_k16(pa, ones, lsum);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int chunk = (2 * nt + ((lq & 3) >> 1)) ^ (vrow & SWZ);
+      const uint2 vb = ds_read_tr16(reinterpret_cast<const uint16_t*>(vr + chunk * 16));
+      o[nt] = mfma_k16(pa, vb, o[nt]);
+    }
+  };
 
-    // ---- online softmax over this iteration's tokens ----------------------------
-    float alpha[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float mx = kNegInf;
-#pragma unroll
-      for (int t = 0; t < KT; ++t) {
-        const float v = kval[t] ? sacc[t][i] * c : kNegInf;
-        sacc[t][i] = v;
-        mx = fmaxf(mx, v);
-      }
-      mx = group_max<16>(mx);
-      const float mnew = fmaxf(mrun[i], mx);
-      const float mref = mnew == kNegInf ? 0.f : mnew;
-      alpha[i] = fast_exp2(mrun[i] - mref);
-      mrun[i] = mnew;
-      float ls = 0.f;
-#pragma unroll
-      for (int t = 0; t < KT; ++t) {
-        const float pr = fast_exp2(sacc[t][i] - mref);
-        sacc[t][i] = pr;
-        ls += pr;
-      }
-      lrun[i] = lrun[i] * alpha[i] + ls;
+  // ---- stream: one stage in flight while the other computes ----------------
+  // The wave's stages are taken in windows whose blocks fit the 64-entry
+  // table register; the pipeline drains at a window's end.
+  constexpr int OPS = 2 * NI;  // load instructions per stage
+  StageBuf<D>* const slot0 = &ring0[wave];
+  StageBuf<D>* const slot1 = &ring1[wave];
+  // Stages per window: an even count whose blocks (plus a block-size
+  // misalignment of the first stage) stay within 64 table entries.
+  const int spwin = ((63 << bs_log2) / kStageTokens) & ~1;
+  for (int w0 = 0; w0 < nst; w0 += spwin) {
+    const int w1 = min(nst, w0 + spwin);
+    tb0 = (ts0 + w0 * kStageTokens) >> bs_log2;
+    {
+      const int lb = tb0 + lane;
+      tbl = (lb < blk_end && lb < a.mb) ? bt[lb] : 0;
     }
-    if (lg < GTP / 4) {
-#pragma unroll
-      for (int t = 0; t < KT; ++t)
-        *reinterpret_cast<float4*>(&pbuf[(16 * t + lq) * GTP + 4 * lg]) =
-            make_float4(sacc[t][0], sacc[t][1], sacc[t][2], sacc[t][3]);
-    }
-    // Rescale the accumulators of heads whose running max moved.
-    float al[GT];
-    bool moved = false;
-#pragma unroll
-    for (int g = 0; g < GT; ++g) {
-      al[g] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[g & 3]), 16 * (g >> 2)));
-      moved |= al[g] != 1.f;
-    }
-    if (moved) {
-#pragma unroll
-      for (int g = 0; g < GT; ++g)
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[g][e] *= al[g];
-    }
-    __builtin_amdgcn_wave_barrier();
-
-    // ---- P.V on VALU: tokens TPW*u + tl and TPW*(u+1) + tl per dot2 ----------
-#pragma unroll
-    for (int u = 0; u < U; u += 2) {
-      const float* pa = &pbuf[(TPW * u + tl) * GTP];
-      const float* pb = &pbuf[(TPW * (u + 1) + tl) * GTP];
-      uint32_t pp[GT];
-#pragma unroll
-      for (int g = 0; g < GT; ++g) pp[g] = pack_bf16x2(pa[g], pb[g]);
-#pragma unroll
-      for (int j = 0; j < CPL; ++j) {
-        const uint32_t* va = reinterpret_cast<const uint32_t*>(&vr[u][j]);
-        const uint32_t* vb = reinterpret_cast<const uint32_t*>(&vr[u + 1][j]);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t lo2 = __builtin_amdgcn_perm(vb[w], va[w], 0x05040100u);
-          const uint32_t hi2 = __builtin_amdgcn_perm(vb[w], va[w], 0x07060302u);
-#pragma unroll
-          for (int g = 0; g < GT; ++g) {
-            acc[g][j * 8 + 2 * w] = dot2_bf16(pp[g], lo2, acc[g][j * 8 + 2 * w]);
-            acc[g][j * 8 + 2 * w + 1] = dot2_bf16(pp[g], hi2, acc[g][j * 8 + 2 * w + 1]);
-          }
-        }
+    vm_wait<0>();  // the window's block ids (and, first time, the query) have arrived
+    uint32_t mask0 = issue(w0, slot0);
+    uint32_t mask1 = w0 + 1 < w1 ? issue(w0 + 1, slot1) : 0u;
+    for (int k = w0; k < w1; k += 2) {
+      if (k + 1 < w1) vm_wait<OPS>(); else vm_wait<0>();
+      compute(slot0, mask0);
+      if (k + 2 < w1) mask0 = issue(k + 2, slot0);
+      if (k + 1 < w1) {
+        if (k + 2 < w1) vm_wait<OPS>(); else vm_wait<0>();
+        compute(slot1, mask1);
+        if (k + 3 < w1) mask1 = issue(k + 3, slot1);
       }
     }
-    __builtin_amdgcn_wave_barrier();
   }
 
-  // Wave totals: sum over the 16 score lanes (l) and over the token lanes (acc).
-  float m[GT], l[GT];
+  // ---- merge the waves and store -------------------------------------------
+  // (max, sum, accumulator) of each wave to LDS, reusing the rings once every
+  // wave is done with them.
+  __syncthreads();
+  float* sm_o = reinterpret_cast<float*>(ring0);   // [nw][16][D]
+  float* sm_ml = reinterpret_cast<float*>(ring1);  // [nw][16][2]
+  static_assert(sizeof(ring0) >= kDecodeWaves * 16 * D * sizeof(float), "merge buffer does not fit");
 #pragma unroll
-  for (int i = 0; i < 4; ++i) lrun[i] = group_sum<16>(lrun[i]);
+  for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-  for (int g = 0; g < GT; ++g) {
-    m[g] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mrun[g & 3]), 16 * (g >> 2)));
-    l[g] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lrun[g & 3]), 16 * (g >> 2)));
-  }
+    for (int i = 0; i < 4; ++i) sm_o[(wave * 16 + 4 * lg + i) * D + 16 * nt + lq] = o[nt][i];
+  if (lg == 0) sm_ml[(wave * 16 + lq) * 2] = mc;
+  if (lq == 0)
 #pragma unroll
-  for (int g = 0; g < GT; ++g)
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      float x = acc[g][e];
-#pragma unroll
-      for (int off = R; off < 64; off <<= 1) x += __shfl_xor(x, off);
-      acc[g][e] = x;
+    for (int i = 0; i < 4; ++i) sm_ml[(wave * 16 + 4 * lg + i) * 2 + 1] = lsum[i];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < GT * D; idx += blockDim.x) {
+    const int g = idx / D;
+    const int d = idx - g * D;
+    float M = kNegInf;
+    for (int w = 0; w < nw; ++w) M = fmaxf(M, sm_ml[(w * 16 + g) * 2]);
+    float L = 0.f, A = 0.f;
+    for (int w = 0; w < nw; ++w) {
+      const float mw = sm_ml[(w * 16 + g) * 2];
+      const float f = mw == kNegInf ? 0.f : fast_exp2(mw - M);
+      L += sm_ml[(w * 16 + g) * 2 + 1] * f;
+      A += sm_o[(w * 16 + g) * D + d] * f;
     }
-  write_partition<2, D, GT, R, CPL>(a, p, b, h0, m, l, acc, sm_acc, sm_m, sm_l);
+    const size_t bh = static_cast<size_t>(b) * a.hq + h0 + g;
+    if (a.out) {
+      store_out<2>(a.out, bh * D + d, L > 0.f ? A / L : 0.f);
+    } else {
+      const size_t slot = bh * a.max_parts + p;
+      a.ws_acc[slot * D + d] = A;
+      if (d == 0) {
+        a.ws_ml[slot * 2] = M;
+        a.ws_ml[slot * 2 + 1] = L;
+      }
+    }
+  }
 }
 
 
@@ -679,30 +743,22 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeParams a) {
     store_out<ESZ>(a.out, static_cast<size_t>(pair) * D + lane + 64 * k, o[k] * inv);
 }
 
-// Tokens one wave processes per iteration, for the kernel a call dispatches to.
-int iter_tokens_rt(int esz, int d, int gt) {
-  if (esz == 2) {
-    switch (d) {
-      case 64: return MfmaGeo<64, 1>::NTOK;
-      case 128: return MfmaGeo<128, 1>::NTOK;
-      default: return MfmaGeo<256, 1>::NTOK;
-    }
-  }
+// Tokens one wave of the fp32 kernel processes per iteration.
+int iter_tokens_f32(int d) {
   return d == 64 ? Geo<4, 64>::ITER : d == 128 ? Geo<4, 128>::ITER : Geo<4, 256>::ITER;
 }
 
 // Query heads one workgroup handles: the largest supported size dividing the
-// group (bf16 kernel: 8, 6, 4, 3, 2, 1; fp32 kernel: 4, 2, 1).
+// group (bf16 kernel: up to 16, the MFMA row count; fp32 kernel: 4, 2, 1).
 int head_group_size(int group, int esz) {
-  static const int kBf16[] = {8, 6, 4, 3, 2, 1};
-  static const int kF32[] = {4, 2, 1};
   if (esz == 2) {
-    for (int g : kBf16)
+    for (int g = 16; g > 1; --g)
       if (group % g == 0) return g;
-  } else {
-    for (int g : kF32)
-      if (group % g == 0) return g;
+    return 1;
   }
+  static const int kF32[] = {4, 2, 1};
+  for (int g : kF32)
+    if (group % g == 0) return g;
   return 1;
 }
 
@@ -728,33 +784,56 @@ int32_t make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, int3
   const int group = hq / hkv;
   pl->gt = head_group_size(group, esz);
   const int32_t span = span_tokens(max_seq_len, window, block_size);
+  const int64_t pairs = static_cast<int64_t>(batch) * hkv * (group / pl->gt);
   int32_t part = partition_tokens;
-  if (part == 0) {
-    const int cus = device_cu_count();
-    if (cus <= 0) return fail(PAGED_ERR_HIP, "cannot query the device compute-unit count");
-    const int64_t wgs_per_part = static_cast<int64_t>(batch) * hkv * (group / pl->gt);
-    part = 64;
-    for (int32_t c = 1024; c >= 64; c >>= 1) {
-      if (wgs_per_part * ((span + c - 1) / c) >= 4LL * cus) {
-        part = c;
-        break;
-      }
+  if (esz == 2) {
+    // Stage-streaming kernel: 16-token stages, four waves per workgroup.
+    const int32_t unit = std::max(kStageTokens, block_size);
+    if (part == 0) {
+      // Aim at every wave slot of the device busy at once (8 waves per CU, 4
+      // at head_dim 256 where a workgroup's rings take most of the LDS) with
+      // whole stages per wave; longer rows get longer partitions.
+      const int cus = device_cu_count();
+      if (cus <= 0) return fail(PAGED_ERR_HIP, "cannot query the device compute-unit count");
+      const int64_t slots = static_cast<int64_t>(head_dim == 256 ? 4 : 8) * cus;
+      const int64_t stages = pairs * ((span + kStageTokens - 1) / kStageTokens);
+      int64_t spw = std::max<int64_t>(1, (stages + slots - 1) / slots);
+      int64_t p2 = 1;
+      while (p2 < spw) p2 <<= 1;
+      part = static_cast<int32_t>(std::min<int64_t>(p2 * kStageTokens * kDecodeWaves, 65536));
+      part = std::max(part, unit);
     }
-    part = std::max(part, block_size);
+    if (part < unit || part > 65536 || part % unit != 0)
+      return fail(PAGED_ERR_INVALID_ARG,
+                  "partition_tokens must be a multiple of %d in [%d, 65536] (got %d)", unit, unit,
+                  part);
+    // Waves per workgroup depend on the partition size only, so a larger
+    // max_seq_len (extra, empty partitions) never changes a row's partials.
+    pl->nw = std::min(kDecodeWaves, part / kStageTokens);
+  } else {
+    if (part == 0) {
+      const int cus = device_cu_count();
+      if (cus <= 0) return fail(PAGED_ERR_HIP, "cannot query the device compute-unit count");
+      part = 64;
+      for (int32_t c = 1024; c >= 64; c >>= 1) {
+        if (pairs * ((span + c - 1) / c) >= 4LL * cus) {
+          part = c;
+          break;
+        }
+      }
+      part = std::max(part, block_size);
+    }
+    if (part < 16 || part > 65536 || part % block_size != 0)
+      return fail(PAGED_ERR_INVALID_ARG,
+                  "partition_tokens must be a multiple of block_size in [16, 65536] (got %d)", part);
+    // Long-lived waves stream best: each wave gets at least 4 iterations of
+    // its partition (1..4 waves), a function of the partition size only.
+    const int iters = (part + iter_tokens_f32(head_dim) - 1) / iter_tokens_f32(head_dim);
+    pl->nw = std::min(kMaxWaves, std::max(1, iters / 4));
   }
-  if (part < 16 || part > 65536 || part % block_size != 0)
-    return fail(PAGED_ERR_INVALID_ARG,
-                "partition_tokens must be a multiple of block_size in [16, 65536] (got %d)", part);
   pl->part = part;
   pl->max_parts = std::max(1, (span + part - 1) / part);
   pl->direct = pl->max_parts == 1;
-  // Waves per workgroup: long-lived waves stream best, so each wave gets at
-  // least 4 iterations of its partition (1..4 waves). The choice depends on
-  // the partition size only, so a larger max_seq_len (extra, empty
-  // partitions) never changes how a row's partials are merged.
-  const int iter = iter_tokens_rt(esz, head_dim, pl->gt);
-  const int iters = (part + iter - 1) / iter;
-  pl->nw = std::min(kMaxWaves, std::max(1, iters / 4));
   pl->ws_bytes = pl->direct ? 0
                             : static_cast<size_t>(batch) * hq * pl->max_parts *
                                   (static_cast<size_t>(head_dim) + 2) * sizeof(float);
@@ -772,24 +851,17 @@ void launch_partial_f32(const DecodeParams& prm, int gt, dim3 grid, dim3 block, 
 }
 
 template <int D>
-void launch_partial_bf16(const DecodeParams& prm, int gt, dim3 grid, dim3 block, hipStream_t s,
+void launch_partial_bf16(const DecodeParams& prm, dim3 grid, dim3 block, hipStream_t s,
                          const LaunchTrace& tr) {
-  switch (gt) {
-    case 8: hipExtLaunchKernelGGL(decode_partial_mfma_kernel<D, 8>, grid, block, 0, s, tr.start(), tr.stop(), 0, prm); break;
-    case 6: hipExtLaunchKernelGGL(decode_partial_mfma_kernel<D, 6>, grid, block, 0, s, tr.start(), tr.stop(), 0, prm); break;
-    case 4: hipExtLaunchKernelGGL(decode_partial_mfma_kernel<D, 4>, grid, block, 0, s, tr.start(), tr.stop(), 0, prm); break;
-    case 3: hipExtLaunchKernelGGL(decode_partial_mfma_kernel<D, 3>, grid, block, 0, s, tr.start(), tr.stop(), 0, prm); break;
-    case 2: hipExtLaunchKernelGGL(decode_partial_mfma_kernel<D, 2>, grid, block, 0, s, tr.start(), tr.stop(), 0, prm); break;
-    default: hipExtLaunchKernelGGL(decode_partial_mfma_kernel<D, 1>, grid, block, 0, s, tr.start(), tr.stop(), 0, prm); break;
-  }
+  hipExtLaunchKernelGGL(decode_partial_lds_kernel<D>, grid, block, 0, s, tr.start(), tr.stop(), 0, prm);
 }
 
 void launch_partial_any(const DecodeParams& prm, int esz, int d, int gt, dim3 grid, dim3 block,
                         hipStream_t s, const LaunchTrace& tr) {
   if (esz == 2) {
-    if (d == 64) launch_partial_bf16<64>(prm, gt, grid, block, s, tr);
-    else if (d == 128) launch_partial_bf16<128>(prm, gt, grid, block, s, tr);
-    else launch_partial_bf16<256>(prm, gt, grid, block, s, tr);
+    if (d == 64) launch_partial_bf16<64>(prm, grid, block, s, tr);
+    else if (d == 128) launch_partial_bf16<128>(prm, grid, block, s, tr);
+    else launch_partial_bf16<256>(prm, grid, block, s, tr);
   } else {
     if (d == 64) launch_partial_f32<64>(prm, gt, grid, block, s, tr);
     else if (d == 128) launch_partial_f32<128>(prm, gt, grid, block, s, tr);
@@ -886,6 +958,7 @@ extern "C" int32_t paged_attn_decode(void* out, const void* q, const void* k_poo
   prm.hq = num_q_heads;
   prm.hkv = num_kv_heads;
   prm.group = num_q_heads / num_kv_heads;
+  prm.gt = pl.gt;
   prm.head_groups = prm.group / pl.gt;
   prm.bs_log2 = ilog2(block_size);
   prm.nb = num_blocks;

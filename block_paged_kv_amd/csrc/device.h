@@ -61,4 +61,30 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+typedef short shortx4_t __attribute__((ext_vector_type(4)));
+
+// Transposing LDS read (ds_read_b64_tr_b16). Within each 16-lane group, lane
+// j receives, for k = 0..3, element j % 4 of the 8-byte row addressed by lane
+// 4k + j / 4: when lane j addresses row r0 + j / 4, columns c0 + 4 (j % 4) ..
+// +3 of a row-major 16-bit matrix, it receives rows r0 .. r0+3 of column
+// c0 + j.
+__device__ __forceinline__ uint2 ds_read_tr16(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) shortx4_t lds_shortx4_t;
+  const shortx4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(p));
+  return __builtin_bit_cast(uint2, r);
+}
+
+// Maximum over the four lanes l % 16 + 16k (k = 0..3) that hold one matrix
+// column of an MFMA 16x16 accumulator: v_permlane32_swap pairs lane l with
+// l ^ 32 and v_permlane16_swap pairs l with l ^ 16; each returns both halves
+// of the pair.
+__device__ __forceinline__ float max_across_groups(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  x = fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+  const unsigned w = __float_as_uint(x);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+}
+
 }  // namespace pagedkv

@@ -55,27 +55,6 @@ struct PrefillParams {
   float scale_log2;
 };
 
-typedef short shortx4_t __attribute__((ext_vector_type(4)));
-
-// Transposing LDS read of four 16-bit values (see the P.V operand comment).
-__device__ __forceinline__ uint2 ds_read_tr16(const uint16_t* p) {
-  typedef __attribute__((address_space(3))) shortx4_t lds_shortx4_t;
-  const shortx4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(p));
-  return __builtin_bit_cast(uint2, r);
-}
-
-// Maximum over the four lanes l % 16 + 16k (k = 0..3) that hold one query
-// row's scores: v_permlane32_swap pairs lane l with l ^ 32 and
-// v_permlane16_swap pairs l with l ^ 16; each returns both halves of the pair.
-__device__ __forceinline__ float max_across_groups(float x) {
-  const unsigned u = __float_as_uint(x);
-  const auto r32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  x = fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
-  const unsigned w = __float_as_uint(x);
-  const auto r16 = __builtin_amdgcn_permlane16_swap(w, w, false, false);
-  return fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
-}
-
 __device__ __forceinline__ floatx4_t mfma16x16x32(const uint4& a, const uint4& b, floatx4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v, a),
                                                  __builtin_bit_cast(bf16x8v, b), c, 0, 0, 0);
