@@ -63,8 +63,8 @@ _SIGNATURES = {
     "paged_last_error": [],
     "paged_kv_write": [_c_void_p] * 5 + [_c_int32] * 6 + [_c_void_p],
     "paged_kv_gather": [_c_void_p] * 5 + [_c_int32, _c_void_p, _c_void_p] + [_c_int32] * 8 + [_c_void_p],
-    "paged_attn_decode_partition_tokens": [_c_int32] * 6 + [_P_I32],
-    "paged_attn_decode_workspace_bytes": [_c_int32] * 8 + [ctypes.POINTER(_c_size)],
+    "paged_attn_decode_partition_tokens": [_c_int32] * 8 + [_P_I32],
+    "paged_attn_decode_workspace_bytes": [_c_int32] * 9 + [ctypes.POINTER(_c_size)],
     "paged_attn_decode": [_c_void_p] * 5 + [_c_int32, _c_void_p] + [_c_int32] * 6 + [_c_float]
     + [_c_int32] * 3 + [_c_void_p, _c_size, _c_int32, _c_void_p],
     "paged_attn_prefill_chunk": [_c_void_p] * 5 + [_c_int32, _c_void_p, _c_void_p] + [_c_int32] * 8
@@ -211,20 +211,34 @@ def paged_kv_gather(out_k, out_v, k_pool, v_pool, block_tables, seq_lens, out_of
         int(sliding_window), _dtype_code(k_pool), _stream(stream)), prepare)
 
 
-def paged_attn_decode_partition_tokens(batch, num_q_heads, num_kv_heads, block_size, max_seq_len,
-                                       sliding_window=0):
+def _dtype_arg(dtype):
+    """PAGED_F32 / PAGED_BF16 from a torch dtype, a name or the code itself."""
+    if isinstance(dtype, int):
+        return dtype
+    name = str(dtype).replace("torch.", "")
+    codes = {"float32": PAGED_F32, "f32": PAGED_F32, "bfloat16": PAGED_BF16, "bf16": PAGED_BF16}
+    if name not in codes:
+        raise PagedError(PAGED_ERR_DTYPE, f"unsupported dtype {dtype}")
+    return codes[name]
+
+
+def paged_attn_decode_partition_tokens(batch, num_q_heads, num_kv_heads, head_dim, block_size,
+                                       max_seq_len, sliding_window=0, dtype="bf16"):
     out = ctypes.c_int32()
-    _check(lib.paged_attn_decode_partition_tokens(batch, num_q_heads, num_kv_heads, block_size,
-                                                  max_seq_len, sliding_window, ctypes.byref(out)))
+    _check(lib.paged_attn_decode_partition_tokens(batch, num_q_heads, num_kv_heads, head_dim,
+                                                  block_size, max_seq_len, sliding_window,
+                                                  _dtype_arg(dtype), ctypes.byref(out)))
     return out.value
 
 
 def paged_attn_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, block_size,
-                                      max_seq_len, sliding_window=0, partition_tokens=0):
+                                      max_seq_len, sliding_window=0, partition_tokens=0,
+                                      dtype="bf16"):
     out = _c_size()
     _check(lib.paged_attn_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim,
                                                  block_size, max_seq_len, sliding_window,
-                                                 partition_tokens, ctypes.byref(out)))
+                                                 partition_tokens, _dtype_arg(dtype),
+                                                 ctypes.byref(out)))
     return out.value
 
 

@@ -666,42 +666,61 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_lds_kernel(D
 
 
 // One wave per (row, query head): combine that pair's partitions in order.
-// Lane p reads partition p's (max, sum) so all of them arrive in one round
-// trip; the accumulators are then summed in partition order with the loads of
-// eight partitions in flight at a time.
+// The row length, the first 64 partitions' (max, sum) and the first 16
+// partitions' accumulators are requested together, before the row's
+// partition count is known (entries past it are fetched but never used), so
+// a typical call needs one round trip to memory before the store. More
+// partitions are summed with eight loads in flight at a time.
 template <int ESZ, int D>
 __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeParams a) {
   constexpr float kNegInf = -INFINITY;
   constexpr int PER_LANE = D / 64;
-  __shared__ float sm_w[4][64];
+  constexpr int PF = 16;
   const int wave = threadIdx.x >> 6;
   const int pair = blockIdx.x * 4 + wave;
   if (pair >= a.batch * a.hq) return;
   const int lane = threadIdx.x & 63;
   const int b = pair / a.hq;
+  const int P = a.max_parts;
+  const float* ml = a.ws_ml + static_cast<size_t>(pair) * P * 2;
+  const float* acc = a.ws_acc + static_cast<size_t>(pair) * P * D;
+
   const int n = a.seq_lens[b];
+  const float mp0 = lane < P ? ml[2 * lane] : kNegInf;
+  const float lp0 = lane < P ? ml[2 * lane + 1] : 0.f;
+  float xf[PF][PER_LANE];
+#pragma unroll
+  for (int q = 0; q < PF; ++q)
+#pragma unroll
+    for (int k = 0; k < PER_LANE; ++k)
+      xf[q][k] = q < P ? acc[static_cast<size_t>(q) * D + lane + 64 * k] : 0.f;
+
   const int lo = a.window > 0 ? max(0, n - a.window) : 0;
   const int s0 = (lo >> a.bs_log2) << a.bs_log2;
-  const int np = n > s0 ? min((n - s0 + a.part - 1) / a.part, a.max_parts) : 0;
-  const float* ml = a.ws_ml + static_cast<size_t>(pair) * a.max_parts * 2;
-  const float* acc = a.ws_acc + static_cast<size_t>(pair) * a.max_parts * D;
+  const int np = n > s0 ? min((n - s0 + a.part - 1) / a.part, P) : 0;
   float o[PER_LANE];
 #pragma unroll
   for (int k = 0; k < PER_LANE; ++k) o[k] = 0.f;
   float L = 0.f;
+  float Mprev = kNegInf;
   for (int p0 = 0; p0 < np; p0 += 64) {
     // (max, sum) of partitions p0 + lane; the running max M covers all chunks.
     const int p = p0 + lane;
-    const float mp = p < np ? ml[2 * p] : kNegInf;
-    const float lp = p < np ? ml[2 * p + 1] : 0.f;
+    float mp, lp;
+    if (p0 == 0) {
+      mp = p < np ? mp0 : kNegInf;
+      lp = p < np ? lp0 : 0.f;
+    } else {
+      mp = p < np ? ml[2 * p] : kNegInf;
+      lp = p < np ? ml[2 * p + 1] : 0.f;
+    }
     float M = mp;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
     // Chunks beyond the first (more than 64 partitions) rescale what came before.
     if (p0 > 0) {
-      const float prevM = sm_w[wave][0];
-      const float newM = fmaxf(prevM, M);
-      const float f = prevM == kNegInf ? 0.f : fast_exp2(prevM - newM);
+      const float newM = fmaxf(Mprev, M);
+      const float f = Mprev == kNegInf ? 0.f : fast_exp2(Mprev - newM);
       L *= f;
 #pragma unroll
       for (int k = 0; k < PER_LANE; ++k) o[k] *= f;
@@ -712,11 +731,19 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeParams a) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) lw += __shfl_xor(lw, off);
     L += lw;
-    __builtin_amdgcn_wave_barrier();
-    sm_w[wave][lane] = w;
-    __builtin_amdgcn_wave_barrier();
     const int cnt = min(64, np - p0);
     int q = 0;
+    if (p0 == 0) {
+#pragma unroll
+      for (int qq = 0; qq < PF; ++qq) {
+        if (qq < cnt) {
+          const float wq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), qq));
+#pragma unroll
+          for (int k = 0; k < PER_LANE; ++k) o[k] = fmaf(xf[qq][k], wq, o[k]);
+        }
+      }
+      q = min(cnt, PF);
+    }
     for (; q + 8 <= cnt; q += 8) {
       float x[8][PER_LANE];
 #pragma unroll
@@ -725,17 +752,19 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeParams a) {
         for (int k = 0; k < PER_LANE; ++k)
           x[i][k] = acc[static_cast<size_t>(p0 + q + i) * D + lane + 64 * k];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < 8; ++i) {
+        const float wq = __shfl(w, q + i);
 #pragma unroll
-        for (int k = 0; k < PER_LANE; ++k) o[k] = fmaf(x[i][k], sm_w[wave][q + i], o[k]);
+        for (int k = 0; k < PER_LANE; ++k) o[k] = fmaf(x[i][k], wq, o[k]);
+      }
     }
-    for (; q < cnt; ++q)
+    for (; q < cnt; ++q) {
+      const float wq = __shfl(w, q);
 #pragma unroll
       for (int k = 0; k < PER_LANE; ++k)
-        o[k] = fmaf(acc[static_cast<size_t>(p0 + q) * D + lane + 64 * k], sm_w[wave][q], o[k]);
-    __builtin_amdgcn_wave_barrier();
-    if (lane == 0) sm_w[wave][0] = M;
-    __builtin_amdgcn_wave_barrier();
+        o[k] = fmaf(acc[static_cast<size_t>(p0 + q) * D + lane + 64 * k], wq, o[k]);
+    }
+    Mprev = M;
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
@@ -787,7 +816,9 @@ int32_t make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, int3
   const int64_t pairs = static_cast<int64_t>(batch) * hkv * (group / pl->gt);
   int32_t part = partition_tokens;
   if (esz == 2) {
-    // Stage-streaming kernel: 16-token stages, four waves per workgroup.
+    // Stage-streaming kernel: 16-token stages, four waves per workgroup
+    // (two or more workgroups per CU, so one's start and merge overlap
+    // another's streaming; eight waves in one workgroup measured slower).
     const int32_t unit = std::max(kStageTokens, block_size);
     if (part == 0) {
       // Aim at every wave slot of the device busy at once (8 waves per CU, 4
@@ -885,13 +916,16 @@ void launch_reduce_d(const DecodeParams& prm, int d, dim3 grid, hipStream_t s, c
 using namespace pagedkv;
 
 extern "C" int32_t paged_attn_decode_partition_tokens(int32_t batch, int32_t num_q_heads,
-                                                      int32_t num_kv_heads, int32_t block_size,
-                                                      int32_t max_seq_len, int32_t sliding_window,
+                                                      int32_t num_kv_heads, int32_t head_dim,
+                                                      int32_t block_size, int32_t max_seq_len,
+                                                      int32_t sliding_window, int32_t dtype,
                                                       int32_t* partition_tokens) {
   if (!partition_tokens) return fail(PAGED_ERR_INVALID_ARG, "NULL argument");
+  const int esz = esize_of(dtype);
+  if (esz == 0) return fail(PAGED_ERR_DTYPE, "unknown dtype %d", dtype);
   Plan pl;
-  if (int32_t rc = make_plan(batch, num_q_heads, num_kv_heads, 128, block_size, max_seq_len,
-                             sliding_window, 0, 2, &pl))
+  if (int32_t rc = make_plan(batch, num_q_heads, num_kv_heads, head_dim, block_size, max_seq_len,
+                             sliding_window, 0, esz, &pl))
     return rc;
   *partition_tokens = pl.part;
   return ok();
@@ -901,11 +935,14 @@ extern "C" int32_t paged_attn_decode_workspace_bytes(int32_t batch, int32_t num_
                                                      int32_t num_kv_heads, int32_t head_dim,
                                                      int32_t block_size, int32_t max_seq_len,
                                                      int32_t sliding_window,
-                                                     int32_t partition_tokens, size_t* bytes) {
+                                                     int32_t partition_tokens, int32_t dtype,
+                                                     size_t* bytes) {
   if (!bytes) return fail(PAGED_ERR_INVALID_ARG, "NULL argument");
+  const int esz = esize_of(dtype);
+  if (esz == 0) return fail(PAGED_ERR_DTYPE, "unknown dtype %d", dtype);
   Plan pl;
   if (int32_t rc = make_plan(batch, num_q_heads, num_kv_heads, head_dim, block_size, max_seq_len,
-                             sliding_window, partition_tokens, 2, &pl))
+                             sliding_window, partition_tokens, esz, &pl))
     return rc;
   *bytes = pl.ws_bytes;
   return ok();

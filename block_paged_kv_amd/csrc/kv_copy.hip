@@ -26,6 +26,9 @@ __global__ __launch_bounds__(kThreads) void kv_write_kernel(
        i += stride) {
     const int64_t t = i / vecs_per_token;
     const int32_t r = static_cast<int32_t>(i - t * vecs_per_token);
+    // The data loads do not depend on the slot: issue all three together.
+    const uint4 kv = new_k[i];
+    const uint4 vv = new_v[i];
     const int64_t slot = slots[t];
     if (slot < 0 || slot >= num_slots) continue;
     const int32_t h = r / vecs_per_head;
@@ -33,8 +36,8 @@ __global__ __launch_bounds__(kThreads) void kv_write_kernel(
     const int64_t blk = slot >> bs_log2;
     const int64_t off = slot & ((1 << bs_log2) - 1);
     const int64_t dst = ((((blk * num_kv_heads + h) << bs_log2) + off) * vecs_per_head) + v;
-    k_pool[dst] = new_k[i];
-    v_pool[dst] = new_v[i];
+    k_pool[dst] = kv;
+    v_pool[dst] = vv;
   }
 }
 

@@ -116,24 +116,29 @@ int32_t paged_kv_gather(void* out_k, void* out_v, const void* k_pool, const void
                         int32_t dtype, void* stream);
 
 /* Partition size (tokens per split-K partition) that paged_attn_decode uses
- * when called with partition_tokens == 0: the largest power of two in
- * [64, 1024] that still gives at least 4 workgroups per compute unit of the
- * current device, else 64. A pure function of its arguments and the device's
- * compute-unit count, so a given call reproduces exactly. */
+ * when called with partition_tokens == 0, for these arguments and dtype.
+ * bf16: the smallest power-of-two multiple of the workgroup's stage span
+ * (16 tokens per wave, 8 waves, 4 at head_dim 256) that keeps every wave
+ * slot of the device busy with whole stages (never below the block size).
+ * fp32: the largest power of two in [64, 1024] that still gives at least 4
+ * workgroups per compute unit, else 64. A pure function of its arguments and
+ * the device's compute-unit count, so a given call reproduces exactly.
+ * Needs a device (PAGED_ERR_HIP otherwise). */
 int32_t paged_attn_decode_partition_tokens(int32_t batch, int32_t num_q_heads,
-                                           int32_t num_kv_heads, int32_t block_size,
-                                           int32_t max_seq_len, int32_t sliding_window,
+                                           int32_t num_kv_heads, int32_t head_dim,
+                                           int32_t block_size, int32_t max_seq_len,
+                                           int32_t sliding_window, int32_t dtype,
                                            int32_t* partition_tokens);
 
-/* Bytes of device workspace paged_attn_decode needs for these arguments
- * (0 when every row fits one partition: the kernel then writes the output
- * directly and no reduce pass runs). partition_tokens == 0 asks for the
- * library rule above (needs a device). */
+/* Bytes of device workspace paged_attn_decode needs for these arguments and
+ * dtype (0 when every row fits one partition: the kernel then writes the
+ * output directly and no reduce pass runs). partition_tokens == 0 asks for
+ * the library rule above (needs a device). */
 int32_t paged_attn_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
                                           int32_t num_kv_heads, int32_t head_dim,
                                           int32_t block_size, int32_t max_seq_len,
                                           int32_t sliding_window, int32_t partition_tokens,
-                                          size_t* bytes);
+                                          int32_t dtype, size_t* bytes);
 
 /* Batched GQA decode over the paged cache: one query token per row, the row's
  * newest (its K/V already written), attending to positions

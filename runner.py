@@ -90,7 +90,7 @@ def gpu_workspace(wl, dev, partition_tokens=None, max_seq_len=None):
     part = wl.partition_tokens if partition_tokens is None else partition_tokens
     msl = wl.max_seq_len if max_seq_len is None else max_seq_len
     need = max(pk.paged_attn_decode_workspace_bytes(wl.batch, wl.hq, wl.hkv, wl.head_dim,
-                                                    wl.block_size, msl, L.window, part)
+                                                    wl.block_size, msl, L.window, part, wl.dtype)
                for L in wl.layers)
     return torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
 

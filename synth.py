@@ -112,8 +112,12 @@ def _suffix_tokens(b, length):
 
 def make(name, *, batch=None, hq=None, hkv=None, head_dim=None, context=None, prefix=None,
          num_blocks=None, seed=None, chunk=None, window=None, dtype=None, part=None,
-         num_prefixes=None, sliding_blocks=None, waves=None):
-    """Build workload ``name`` at its published sizes; keyword overrides shrink it for tests."""
+         num_prefixes=None, sliding_blocks=None, waves=None, block_size=None):
+    """Build workload ``name`` at its published sizes; keyword overrides shrink it for tests.
+
+    ``block_size`` (a power of two in [8, 64], default 16) changes only the paging:
+    the random draws are the same, prefix lengths round to whole blocks."""
+    bs = BLOCK_SIZE if block_size is None else int(block_size)
     seed = SEEDS[name] if seed is None else seed
     rng = np.random.default_rng(seed)
 
@@ -125,7 +129,7 @@ def make(name, *, batch=None, hq=None, hkv=None, head_dim=None, context=None, pr
         lens = np.array(context if context is not None else [40, 75][:B], dtype=np.int32)
         pre = 32 if prefix is None else prefix
         return _decode_from_prefixes(name, rng, B, Hq, Hkv, D, bf16, lens, [pre], [0] * B,
-                                     [("main", NB, 0, None, free)], part or 0)
+                                     [("main", NB, 0, None, free)], part or 0, bs=bs)
 
     if name == "qwen3":
         # ``waves`` > 1 stacks that many independent batches (each with its own
@@ -139,7 +143,7 @@ def make(name, *, batch=None, hq=None, hkv=None, head_dim=None, context=None, pr
         pre = 512 if prefix is None else prefix
         wl = _decode_from_prefixes(name, rng, B * R, Hq, Hkv, D, (dtype or "bf16") == "bf16", lens,
                                    [pre] * R, [b // B for b in range(B * R)],
-                                   [("main", NB, 0, None, free)], part or 0)
+                                   [("main", NB, 0, None, free)], part or 0, bs=bs)
         wl.wave_size = B
         return wl
 
@@ -151,11 +155,11 @@ def make(name, *, batch=None, hq=None, hkv=None, head_dim=None, context=None, pr
         lens = rng.integers(lo, hi + 1, size=B).astype(np.int32)
         npre = num_prefixes or 4
         pmax = 1024 if prefix is None else prefix
-        pre_lens = [int(BLOCK_SIZE * (x // BLOCK_SIZE)) for x in rng.integers(0, pmax + 1, size=npre)]
+        pre_lens = [int(bs * (x // bs)) for x in rng.integers(0, pmax + 1, size=npre)]
         choice = [int(c) for c in rng.integers(0, npre, size=B)]
         return _decode_from_prefixes(name, rng, B, Hq, Hkv, D, (dtype or "bf16") == "bf16", lens,
                                      pre_lens, choice, [("main", NB, 0, None, free)],
-                                     512 if part is None else part)
+                                     512 if part is None else part, bs=bs)
 
     if name == "hybrid":
         B, Hq, Hkv, D = batch or 8, hq or 8, hkv or 1, head_dim or 256
@@ -169,7 +173,7 @@ def make(name, *, batch=None, hq=None, hkv=None, head_dim=None, context=None, pr
         layers = [("sliding", NBS, W, None, free_slide), ("full", NB, 0, None, free_full),
                   ("shared", NB, 0, "full", None)]
         return _decode_from_prefixes(name, rng, B, Hq, Hkv, D, (dtype or "bf16") == "bf16", lens,
-                                     [0], [0] * B, layers, part or 0)
+                                     [0], [0] * B, layers, part or 0, bs=bs)
 
     if name == "prefill":
         B, Hq, Hkv, D = batch or 1, hq or 32, hkv or 8, head_dim or 128
@@ -191,12 +195,13 @@ def make(name, *, batch=None, hq=None, hkv=None, head_dim=None, context=None, pr
             layer.k[b] = np.concatenate([layer.k[b], _normal(rng, (int(C[b]), Hkv, D), True)])
             layer.v[b] = np.concatenate([layer.v[b], _normal(rng, (int(C[b]), Hkv, D), True)])
         return Workload(name, "prefill", B, Hq, Hkv, D, "bf16", lens, toks, [layer],
-                        1.0 / math.sqrt(D), chunk_lens=C)
+                        1.0 / math.sqrt(D), chunk_lens=C, block_size=bs)
 
     raise ValueError(f"unknown workload {name}")
 
 
-def _decode_from_prefixes(name, rng, B, Hq, Hkv, D, bf16, lens, pre_lens, choice, layer_specs, part):
+def _decode_from_prefixes(name, rng, B, Hq, Hkv, D, bf16, lens, pre_lens, choice, layer_specs, part,
+                          bs=BLOCK_SIZE):
     layers = [Layer(nm, nb, w, alias, free) for nm, nb, w, alias, free in layer_specs]
     toks = []
     for b in range(B):
@@ -214,7 +219,7 @@ def _decode_from_prefixes(name, rng, B, Hq, Hkv, D, bf16, lens, pre_lens, choice
             n = int(lens[b])
             start = 0
             if L.window:
-                start = (max(0, n - L.window) // BLOCK_SIZE) * BLOCK_SIZE
+                start = (max(0, n - L.window) // bs) * bs
             plen = min(pre_lens[choice[b]], n - 1)
             body_from = max(start, plen)
             ks = [pk[choice[b]][0][start:plen]] if start < plen else []
@@ -235,7 +240,7 @@ def _decode_from_prefixes(name, rng, B, Hq, Hkv, D, bf16, lens, pre_lens, choice
             L.k[b] = np.concatenate([L.k[b], _normal(rng, (1, Hkv, D), bf16)])
             L.v[b] = np.concatenate([L.v[b], _normal(rng, (1, Hkv, D), bf16)])
     return Workload(name, "decode", B, Hq, Hkv, D, "bf16" if bf16 else "f32", lens, toks, layers,
-                    1.0 / math.sqrt(D), partition_tokens=part)
+                    1.0 / math.sqrt(D), partition_tokens=part, block_size=bs)
 
 
 # --------------------------------------------------------------------- tables

@@ -86,21 +86,35 @@ def test_prefill_argument_errors():
         assert rc == pk.PAGED_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("B,hq,hkv,d,msl,w,part", [
-    (4, 16, 8, 128, 2048, 0, 128), (32, 32, 8, 128, 8192, 0, 512), (8, 8, 1, 256, 32768, 512, 64),
-    (2, 4, 2, 64, 75, 0, 16), (3, 6, 3, 64, 100, 0, 128)])
-def test_workspace_bytes(B, hq, hkv, d, msl, w, part):
+@pytest.mark.parametrize("B,hq,hkv,d,msl,w,part,dt", [
+    (4, 16, 8, 128, 2048, 0, 128, "bf16"), (32, 32, 8, 128, 8192, 0, 512, "bf16"),
+    (8, 8, 1, 256, 32768, 512, 64, "bf16"), (2, 4, 2, 64, 75, 0, 16, "f32"),
+    (3, 6, 3, 64, 100, 0, 128, "bf16"), (2, 4, 2, 64, 75, 0, 48, "f32")])
+def test_workspace_bytes(B, hq, hkv, d, msl, w, part, dt):
     span = min(msl, w + 15) if w else msl
     parts = -(-span // part)
     expect = 0 if parts == 1 else B * hq * parts * (d + 2) * 4
-    assert pk.paged_attn_decode_workspace_bytes(B, hq, hkv, d, 16, msl, w, part) == expect
+    assert pk.paged_attn_decode_workspace_bytes(B, hq, hkv, d, 16, msl, w, part, dt) == expect
+
+
+def test_partition_must_fit_the_kernel():
+    # bf16 partitions are whole 16-token stages; fp32 ones whole blocks
+    with pytest.raises(pk.PagedError):
+        pk.paged_attn_decode_workspace_bytes(2, 4, 2, 64, 8, 100, 0, 24, "bf16")
+    assert pk.paged_attn_decode_workspace_bytes(2, 4, 2, 64, 8, 100, 0, 24, "f32") > 0
+    with pytest.raises(pk.PagedError) as e:
+        pk.paged_attn_decode_workspace_bytes(2, 4, 2, 64, 16, 100, 0, 64, "f16")
+    assert e.value.code == pk.PAGED_ERR_DTYPE
 
 
 def test_library_rule_needs_a_device_here():
     # No GPU in this container: the rule's device query fails cleanly.
     with pytest.raises(pk.PagedError) as e:
-        pk.paged_attn_decode_partition_tokens(4, 16, 8, 16, 2048, 0)
-    assert e.value.code in (pk.PAGED_ERR_HIP, pk.PAGED_OK) or e.value.code == pk.PAGED_ERR_HIP
+        pk.paged_attn_decode_partition_tokens(4, 16, 8, 128, 16, 2048, 0)
+    assert e.value.code == pk.PAGED_ERR_HIP
+    with pytest.raises(pk.PagedError) as e:
+        pk.paged_attn_decode_workspace_bytes(4, 16, 8, 128, 16, 2048, 0, 0, "f32")
+    assert e.value.code == pk.PAGED_ERR_HIP
 
 
 def test_trace_api_without_launches():

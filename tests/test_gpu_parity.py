@@ -80,6 +80,9 @@ def run_case(pk, wl, rows=None, label="", **step_kw):
     ("hybrid", dict(batch=3, context=700, window=64, sliding_blocks=40, num_blocks=200)),
     ("prefill", dict(batch=3, context=[70, 33, 0], chunk=[40, 9, 17], num_blocks=64)),
     ("mixed", dict(batch=5, context=(20, 300), prefix=100, num_blocks=200, head_dim=256, hq=4, hkv=2)),
+    ("mixed", dict(batch=5, context=(20, 300), prefix=100, num_blocks=300, block_size=8)),
+    ("hybrid", dict(batch=2, context=500, window=100, hq=8, hkv=1, head_dim=256, sliding_blocks=30,
+                    num_blocks=100, block_size=64)),
 ])
 def test_write_is_bit_exact(pk, name, kw):
     import torch
@@ -118,6 +121,9 @@ def test_write_skips_padding_and_out_of_range_slots(pk):
     ("tiny", {}),
     ("mixed", dict(batch=6, context=(20, 300), prefix=100, num_blocks=300)),
     ("hybrid", dict(batch=3, context=700, window=64, sliding_blocks=40, num_blocks=200)),
+    ("hybrid", dict(batch=2, context=500, window=100, hq=4, hkv=2, head_dim=128, sliding_blocks=60,
+                    num_blocks=200, block_size=8)),
+    ("mixed", dict(batch=5, context=(1, 400), prefix=100, num_blocks=200, block_size=32)),
 ])
 def test_gather_returns_flat_kv(pk, name, kw):
     import torch
@@ -166,6 +172,33 @@ DECODE_SMALL = [
     ("hybrid", dict(batch=3, context=700, window=1, sliding_blocks=40, num_blocks=200), {}),
     ("hybrid", dict(batch=2, context=300, window=100, hq=4, hkv=2, head_dim=128, sliding_blocks=40, num_blocks=100), dict(partition_tokens=32)),
 ]
+
+
+# Block sizes other than 16: two blocks per 16-token stage (8) and stages inside
+# a block (32, 64), with partitions and windows that start mid-block.
+DECODE_BLOCK_SIZES = [
+    ("mixed", dict(batch=5, context=(1, 400), prefix=100, num_blocks=400, block_size=8), dict(partition_tokens=64)),
+    ("mixed", dict(batch=5, context=(1, 400), prefix=100, num_blocks=400, block_size=8), {}),
+    ("mixed", dict(batch=5, context=(1, 400), prefix=100, num_blocks=200, block_size=32), {}),
+    ("mixed", dict(batch=5, context=(1, 700), prefix=130, num_blocks=100, block_size=64), dict(partition_tokens=128)),
+    ("mixed", dict(batch=4, hq=6, hkv=2, head_dim=64, context=(1, 300), prefix=40, num_blocks=200, block_size=32), {}),
+    ("mixed", dict(batch=3, hq=4, hkv=2, head_dim=64, dtype="f32", context=(30, 300), prefix=40, num_blocks=200,
+                   block_size=8), {}),
+    ("mixed", dict(batch=3, hq=4, hkv=2, head_dim=128, dtype="f32", context=(30, 300), prefix=40, num_blocks=100,
+                   block_size=64), dict(partition_tokens=64)),
+    ("hybrid", dict(batch=2, context=500, window=100, hq=4, hkv=2, head_dim=128, sliding_blocks=60, num_blocks=200,
+                    block_size=8), {}),
+    ("hybrid", dict(batch=2, context=500, window=100, hq=8, hkv=1, head_dim=256, sliding_blocks=30, num_blocks=100,
+                    block_size=64), {}),
+    ("hybrid", dict(batch=2, context=500, window=37, hq=4, hkv=2, head_dim=128, sliding_blocks=30, num_blocks=100,
+                    block_size=32), dict(partition_tokens=32)),
+]
+
+
+@pytest.mark.parametrize("name,kw,step", DECODE_BLOCK_SIZES,
+                         ids=[f"{n}-bs{kw['block_size']}-{i}" for i, (n, kw, _) in enumerate(DECODE_BLOCK_SIZES)])
+def test_decode_block_sizes(pk, name, kw, step):
+    run_case(pk, synth.make(name, **kw), label="decode-block-size", **step)
 
 
 @pytest.mark.parametrize("name,kw,step", DECODE_SMALL,
@@ -256,6 +289,9 @@ PREFILL_SMALL = [
     dict(batch=2, context=[100, 64], chunk=[64, 100], num_blocks=64, hq=4, hkv=1, head_dim=256),
     dict(batch=2, context=[300, 64], chunk=[150, 100], num_blocks=64, window=37),
     dict(batch=1, context=[500], chunk=[129], num_blocks=64, window=200, hq=4, hkv=4),
+    dict(batch=2, context=[100, 37], chunk=[40, 20], num_blocks=64, block_size=8),
+    dict(batch=2, context=[100, 37], chunk=[40, 20], num_blocks=64, block_size=32, window=45),
+    dict(batch=2, context=[300, 5], chunk=[200, 130], num_blocks=64, block_size=64),
 ]
 
 
