@@ -444,6 +444,32 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_lds_kernel(D
   const int lq = lane & 15;
   const int lg = lane >> 4;
 
+  const int bs_log2 = a.bs_log2;
+  const int bs_mask = (1 << bs_log2) - 1;
+  const bool bs8 = bs_log2 == 3;
+  const int nst_part = a.part / kStageTokens;
+  const int spw = (nst_part + nw - 1) / nw;  // stages per wave
+
+  // Query heads h0 .. h0+GT-1 as the B operand of S^T = K Q^T: lane (lq, lg)
+  // holds head lq, head_dim elements 32*ks + 8*lg .. +8. Requested before the
+  // row length is known, as is (without a window, where a partition's start
+  // does not depend on the row length) the wave's first table window.
+  uint4 qb[KS];
+  {
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
+                           (static_cast<size_t>(b) * a.hq + h0 + (lq < GT ? lq : 0)) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qb[ks] = lq < GT ? *reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * lg) : make_uint4(0, 0, 0, 0);
+  }
+  const int32_t* bt = a.bt + static_cast<size_t>(b) * a.mb;
+  const bool spec_tbl = a.window == 0;
+  int tbl_first = 0;
+  if (spec_tbl) {
+    const int lb = ((p * a.part + wave * spw * kStageTokens) >> bs_log2) + lane;
+    tbl_first = lb < a.mb ? bt[lb] : 0;
+  }
+
   if (ps >= n) {
     // Only an empty row (n == 0) reaches this with p == 0: its output is zero.
     if (a.out && p == 0)
@@ -453,32 +479,15 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_lds_kernel(D
   }
   const int t_begin = max(ps, lo);
   const int t_end = min(ps + a.part, n);
-  const int bs_log2 = a.bs_log2;
-  const int bs_mask = (1 << bs_log2) - 1;
-  const bool bs8 = bs_log2 == 3;
 
   // This wave's stages: a contiguous share of the partition's 16-token
   // stages, clipped to those that touch [t_begin, t_end).
-  const int nst_part = a.part / kStageTokens;
-  const int spw = (nst_part + nw - 1) / nw;
   const int k_first = max(wave * spw, (t_begin - ps) / kStageTokens);
   const int k_last = min(min((wave + 1) * spw, nst_part), (t_end - ps + kStageTokens - 1) / kStageTokens);
   const int nst = max(0, k_last - k_first);  // stages this wave computes
   const int ts0 = ps + k_first * kStageTokens;
 
-  // Query heads h0 .. h0+GT-1 as the B operand of S^T = K Q^T: lane (lq, lg)
-  // holds head lq, head_dim elements 32*ks + 8*lg .. +8.
-  uint4 qb[KS];
-  {
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
-                           (static_cast<size_t>(b) * a.hq + h0 + (lq < GT ? lq : 0)) * D;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qb[ks] = lq < GT ? *reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * lg) : make_uint4(0, 0, 0, 0);
-  }
-
   // Block-table window: lane i holds the entry of block tb0 + i.
-  const int32_t* bt = a.bt + static_cast<size_t>(b) * a.mb;
   const int blk_end = nst > 0 ? ((ts0 + nst * kStageTokens - 1) >> bs_log2) + 1 : 0;
   int tb0 = 0;
   int tbl = 0;
@@ -591,7 +600,11 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_lds_kernel(D
     }
   };
 
-  // ---- stream: one stage in flight while the other computes ----------------
+  // ---- stream: one stage landing while the other computes ------------------
+  // Two stages of each wave are in flight at the start of a window; stage
+  // k+2 is requested once stage k is consumed. (Requesting stage k+1 only
+  // once stage k has landed keeps less in flight and measured faster for
+  // 4096-token partitions, slower for the 512-token ones of the mixed batch.)
   // The wave's stages are taken in windows whose blocks fit the 64-entry
   // table register; the pipeline drains at a window's end.
   constexpr int OPS = 2 * NI;  // load instructions per stage
@@ -603,7 +616,9 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_lds_kernel(D
   for (int w0 = 0; w0 < nst; w0 += spwin) {
     const int w1 = min(nst, w0 + spwin);
     tb0 = (ts0 + w0 * kStageTokens) >> bs_log2;
-    {
+    if (w0 == 0 && spec_tbl) {
+      tbl = tbl_first;  // requested at the start: without a window ts0 = ps + wave * spw * 16
+    } else {
       const int lb = tb0 + lane;
       tbl = (lb < blk_end && lb < a.mb) ? bt[lb] : 0;
     }
