@@ -12,17 +12,20 @@ computes, written from the mlx-node paged-cache and perf documentation pages
 * ``attention`` -- slot-mapped KV write, block-table gather, decode attention
   and chunked-prefill attention, in float64 after materialising each
   request's contiguous K/V from its block table.
+* ``fp8`` -- the FP8 (E4M3) KV cache encoding: encode, decode and the
+  per-layer-scale quantization a write applies.
 * ``allocator`` -- ``RefAllocator``, the host block allocator (refcounts,
   prefix table, LRU eviction, null sentinel), written from the written policy,
   not from the C++ library.
 
 Every function here is pinned by the ``-m "not gpu"`` tests in
 ``tests/test_oracle_pins.py`` and ``tests/test_ref_allocator.py`` against
-closed forms, hand-worked fixtures in ``tests/golden/`` and invariants.
+closed forms, hand-worked fixtures in ``tests/golden/`` and invariants, and
+``fp8`` by ``tests/test_oracle_fp8.py``.
 Nothing here is "parity unpinned".
 """
 
-from . import attention, allocator  # noqa: F401
+from . import attention, allocator, fp8  # noqa: F401
 from .attention import (  # noqa: F401
     kv_write,
     gather_positions,
