@@ -30,6 +30,7 @@ PAGED_ERR_HIP = -6
 
 PAGED_F32 = 0
 PAGED_BF16 = 1
+PAGED_FP8_E4M3 = 2
 
 KERNELS = {
     "kv_write": 0,
@@ -63,6 +64,11 @@ _SIGNATURES = {
     "paged_last_error": [],
     "paged_kv_write": [_c_void_p] * 5 + [_c_int32] * 6 + [_c_void_p],
     "paged_kv_gather": [_c_void_p] * 5 + [_c_int32, _c_void_p, _c_void_p] + [_c_int32] * 8 + [_c_void_p],
+    "paged_kv_write_fp8": [_c_void_p] * 5 + [_c_int32] * 6 + [_c_float] * 2 + [_c_void_p],
+    "paged_attn_decode_fp8": [_c_void_p] * 5 + [_c_int32, _c_void_p] + [_c_int32] * 6 + [_c_float] * 3
+    + [_c_int32] * 3 + [_c_void_p, _c_size, _c_void_p],
+    "paged_attn_prefill_chunk_fp8": [_c_void_p] * 5 + [_c_int32, _c_void_p, _c_void_p] + [_c_int32] * 8
+    + [_c_float] * 3 + [_c_int32, _c_void_p],
     "paged_attn_decode_partition_tokens": [_c_int32] * 8 + [_P_I32],
     "paged_attn_decode_workspace_bytes": [_c_int32] * 9 + [ctypes.POINTER(_c_size)],
     "paged_attn_decode": [_c_void_p] * 5 + [_c_int32, _c_void_p] + [_c_int32] * 6 + [_c_float]
@@ -150,6 +156,8 @@ def _dtype_code(t):
         return PAGED_BF16
     if t.dtype == torch.float32:
         return PAGED_F32
+    if t.dtype == torch.float8_e4m3fn:
+        return PAGED_FP8_E4M3
     raise PagedError(PAGED_ERR_DTYPE, f"unsupported tensor dtype {t.dtype}")
 
 
@@ -216,7 +224,8 @@ def _dtype_arg(dtype):
     if isinstance(dtype, int):
         return dtype
     name = str(dtype).replace("torch.", "")
-    codes = {"float32": PAGED_F32, "f32": PAGED_F32, "bfloat16": PAGED_BF16, "bf16": PAGED_BF16}
+    codes = {"float32": PAGED_F32, "f32": PAGED_F32, "bfloat16": PAGED_BF16, "bf16": PAGED_BF16,
+             "float8_e4m3fn": PAGED_FP8_E4M3, "fp8": PAGED_FP8_E4M3}
     if name not in codes:
         raise PagedError(PAGED_ERR_DTYPE, f"unsupported dtype {dtype}")
     return codes[name]
@@ -285,6 +294,72 @@ def paged_attn_prefill_chunk(out, q, k_pool, v_pool, block_tables, cu_q_lens, se
         _dev(cu_q_lens, "cu_q_lens", torch.int32, 1), _dev(seq_lens, "seq_lens", torch.int32, 1),
         B, T, int(max_q_len), hq, hkv, d, bs, nb, float(scale), int(sliding_window),
         _dtype_code(q), _stream(stream)), prepare)
+
+
+# ------------------------------------------------------------------ FP8 KV pools
+def _fp8_pools(k_pool, v_pool):
+    torch = _torch()
+    geom = _pool_geom(k_pool, v_pool)
+    if k_pool.dtype != torch.float8_e4m3fn:
+        raise PagedError(PAGED_ERR_DTYPE, f"FP8 pools must be torch.float8_e4m3fn, got {k_pool.dtype}")
+    return geom
+
+
+def paged_kv_write_fp8(k_pool, v_pool, new_k, new_v, slot_mapping, k_scale, v_scale, stream=None,
+                       prepare=False):
+    """Quantizing write: ``new_k/new_v [T, Hkv, D]`` (bf16 or f32) into float8_e4m3fn pools."""
+    torch = _torch()
+    nb, hkv, bs, d = _fp8_pools(k_pool, v_pool)
+    T = int(slot_mapping.shape[0])
+    for name, t in (("new_k", new_k), ("new_v", new_v)):
+        if tuple(t.shape) != (T, hkv, d) or t.dtype != new_k.dtype:
+            raise PagedError(PAGED_ERR_INVALID_ARG, f"{name} must be [{T}, {hkv}, {d}] like new_k")
+    return _invoke(lib.paged_kv_write_fp8, (
+        _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), _dev(new_k, "new_k"), _dev(new_v, "new_v"),
+        _dev(slot_mapping, "slot_mapping", torch.int64, 1), T, nb, bs, hkv, d,
+        _dtype_code(new_k), float(k_scale), float(v_scale), _stream(stream)), prepare)
+
+
+def paged_attn_decode_fp8(out, q, k_pool, v_pool, block_tables, seq_lens, scale, k_scale, v_scale,
+                          max_seq_len, sliding_window=0, partition_tokens=0, workspace=None,
+                          stream=None, prepare=False):
+    """GQA decode over float8_e4m3fn pools; ``out, q [B, Hq, D]`` bf16."""
+    torch = _torch()
+    nb, hkv, bs, d = _fp8_pools(k_pool, v_pool)
+    B, hq, dq = (int(x) for x in q.shape)
+    if dq != d or tuple(out.shape) != (B, hq, d) or q.dtype != torch.bfloat16 or out.dtype != q.dtype:
+        raise PagedError(PAGED_ERR_INVALID_ARG, "q/out must be [B, Hq, D] bf16")
+    if block_tables.dim() != 2 or int(block_tables.shape[0]) != B or tuple(seq_lens.shape) != (B,):
+        raise PagedError(PAGED_ERR_INVALID_ARG, "block_tables must be [B, MB] and seq_lens [B]")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    return _invoke(lib.paged_attn_decode_fp8, (
+        _dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+        _dev(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
+        _dev(seq_lens, "seq_lens", torch.int32, 1), B, hq, hkv, d, bs, nb, float(scale),
+        float(k_scale), float(v_scale), int(sliding_window), int(partition_tokens), int(max_seq_len),
+        ws_ptr, ws_bytes, _stream(stream)), prepare)
+
+
+def paged_attn_prefill_chunk_fp8(out, q, k_pool, v_pool, block_tables, cu_q_lens, seq_lens,
+                                 max_q_len, scale, k_scale, v_scale, sliding_window=0, stream=None,
+                                 prepare=False):
+    """Chunked prefill over float8_e4m3fn pools; ``out, q [T, Hq, D]`` bf16."""
+    torch = _torch()
+    nb, hkv, bs, d = _fp8_pools(k_pool, v_pool)
+    T, hq, dq = (int(x) for x in q.shape)
+    B = int(seq_lens.shape[0])
+    if dq != d or tuple(out.shape) != (T, hq, d) or q.dtype != torch.bfloat16 or out.dtype != q.dtype:
+        raise PagedError(PAGED_ERR_INVALID_ARG, "q/out must be [T, Hq, D] bf16")
+    if tuple(cu_q_lens.shape) != (B + 1,) or block_tables.dim() != 2 or int(block_tables.shape[0]) != B:
+        raise PagedError(PAGED_ERR_INVALID_ARG, "cu_q_lens must be [B+1] and block_tables [B, MB]")
+    return _invoke(lib.paged_attn_prefill_chunk_fp8, (
+        _dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+        _dev(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
+        _dev(cu_q_lens, "cu_q_lens", torch.int32, 1), _dev(seq_lens, "seq_lens", torch.int32, 1),
+        B, T, int(max_q_len), hq, hkv, d, bs, nb, float(scale), float(k_scale), float(v_scale),
+        int(sliding_window), _stream(stream)), prepare)
 
 
 # ------------------------------------------------------------------ tracing

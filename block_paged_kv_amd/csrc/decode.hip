@@ -59,7 +59,8 @@ struct DecodeParams {
   const int32_t* bt;
   const int32_t* seq_lens;
   int32_t batch, mb, hq, hkv, group, gt, head_groups, bs_log2, nb, window, part, max_parts;
-  float scale_log2;  // scale * log2(e)
+  float scale_log2;  // scale * log2(e) (times the K scale for FP8 pools)
+  float v_scale;     // FP8 pools: the V scale; 1 otherwise
 };
 
 template <int ESZ>
@@ -359,16 +360,26 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodePa
 //   * Online softmax in scaled log2 units with lazy rescaling (the reference
 //     max moves only when a score exceeds it by 2^8); the partition's
 //     (max, sum, accumulator) are exact for whatever reference is kept.
-template <int D>
+// Stage geometry for head_dim D and KV elements of ESZ bytes (2: bf16,
+// 1: FP8 E4M3 codes).
+template <int D, int ESZ>
 struct StageGeo {
-  static constexpr int ROWB = D * 2;            // bytes per token row
-  static constexpr int CPT = D / 8;             // 16-byte chunks per token row
+  static constexpr int ROWB = D * ESZ;          // bytes per token row in the pool
+  static constexpr int EPC = 16 / ESZ;          // elements per 16-byte chunk
+  static constexpr int CPT = ROWB / 16;         // 16-byte chunks per token row
   static constexpr int TPI = 1024 / ROWB;       // token rows per load instruction (1 KiB)
   static constexpr int NI = 16 / TPI;           // load instructions per stage, K (and V)
   static constexpr int SBYTES = 16 * ROWB;      // K (or V) bytes of one stage
   static constexpr int KS = D / 32;             // q.K k-steps
   static constexpr int NT = D / 16;             // output column tiles
   static constexpr int SWZ = CPT < 16 ? CPT - 1 : 15;  // row bits folded into the chunk index
+  // bf16 V rows read by the transposing P.V operand load (FP8 stages are
+  // widened into such a tile first).
+  static constexpr int VROWB = D * 2;
+  static constexpr int VSWZ = (VROWB / 16) < 16 ? (VROWB / 16) - 1 : 15;
+  // Ring slot 0 doubles as the wave-merge buffer (16 heads x D floats).
+  static constexpr int MERGE = 16 * D * 4;
+  static constexpr int SLOT0 = 2 * SBYTES > MERGE ? 2 * SBYTES : MERGE;
 };
 
 constexpr int kStageTokens = 16;
@@ -409,24 +420,22 @@ __device__ __forceinline__ void vm_wait() {
   asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
 
-// One stage buffer: K rows then V rows.
-template <int D>
-struct StageBuf {
-  uint4 k[StageGeo<D>::SBYTES / 16];
-  uint4 v[StageGeo<D>::SBYTES / 16];
-};
-
-template <int D>
+template <int D, int ESZ>
 __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_lds_kernel(DecodeParams a) {
-  using Sg = StageGeo<D>;
+  using Sg = StageGeo<D, ESZ>;
+  constexpr bool KV8 = ESZ == 1;
   constexpr int CPT = Sg::CPT, TPI = Sg::TPI, NI = Sg::NI, KS = Sg::KS, NT = Sg::NT;
-  constexpr int ROWB = Sg::ROWB, SWZ = Sg::SWZ;
+  constexpr int ROWB = Sg::ROWB, SWZ = Sg::SWZ, EPC = Sg::EPC, SBYTES = Sg::SBYTES;
+  constexpr int VROWB = Sg::VROWB, VSWZ = Sg::VSWZ;
   constexpr float kNegInf = -INFINITY;
 
-  // One ring slot per array, so the compiler can tell the slots apart when it
-  // orders LDS reads against the loads still writing other slots.
-  __shared__ StageBuf<D> ring0[kDecodeWaves];
-  __shared__ StageBuf<D> ring1[kDecodeWaves];
+  // One ring slot per array (K rows then V rows), so the compiler can tell the
+  // slots apart when it orders LDS reads against the loads still writing
+  // other slots. Slot 0 is padded to hold the wave-merge buffer.
+  __shared__ uint4 ring0[kDecodeWaves][Sg::SLOT0 / 16];
+  __shared__ uint4 ring1[kDecodeWaves][2 * SBYTES / 16];
+  // FP8: each wave's V stage widened to bf16 rows for the transposing read.
+  __shared__ uint4 vwide[KV8 ? kDecodeWaves : 1][KV8 ? 16 * VROWB / 16 : 1];
 
   const int p = blockIdx.x;
   const int hg = blockIdx.y;
@@ -500,17 +509,17 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_lds_kernel(D
   for (int i = 0; i < NI; ++i) {
     const int row = i * TPI + lane / CPT;
     const int chunk = (lane % CPT) ^ (row & SWZ);
-    lane_off[i] = static_cast<uint32_t>((row & (bs8 ? 7 : 15)) * D + chunk * 8);
+    lane_off[i] = static_cast<uint32_t>((row & (bs8 ? 7 : 15)) * D + chunk * EPC);
   }
-  const uint16_t* kpool = static_cast<const uint16_t*>(a.k_pool);
-  const uint16_t* vpool = static_cast<const uint16_t*>(a.v_pool);
+  const char* kpool = static_cast<const char*>(a.k_pool);
+  const char* vpool = static_cast<const char*>(a.v_pool);
 
   // Issue the loads of stage k (0-based within this wave) into ring slot sb:
   // exactly 2*NI load instructions, every lane active (rows the stage does
   // not attend read the zero chunk). Returns the stage's valid-token mask
   // (bit t: token ts + t is attended and its block id is valid). The block
   // ids come from the table window, loaded before any stage is in flight.
-  auto issue = [&](int k, StageBuf<D>* sb) -> uint32_t {
+  auto issue = [&](int k, uint4* sb) -> uint32_t {
     const int ts = ts0 + k * kStageTokens;
     const int blk = ts >> bs_log2;
     const int phys_lo = __builtin_amdgcn_readlane(tbl, blk - tb0);
@@ -528,12 +537,16 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_lds_kernel(D
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const size_t base = (bs8 && i * TPI >= 8) ? base_hi : base_lo;
-      const bool ok = (vmask >> (i * TPI + lane / CPT)) & 1u;
-      const void* ksrc = ok ? static_cast<const void*>(kpool + base + lane_off[i]) : &kZeroChunk;
-      const void* vsrc = ok ? static_cast<const void*>(vpool + base + lane_off[i]) : &kZeroChunk;
-      lds_dma16(ksrc, &sb->k[i * 64]);
-      lds_dma16(vsrc, &sb->v[i * 64]);
+      // Row i*TPI + lane/CPT of the stage; with block size 8, rows 8..15 are in
+      // the second block (one instruction covers both at 64-byte rows).
+      const int row = i * TPI + lane / CPT;
+      const size_t base = (bs8 && row >= 8) ? base_hi : base_lo;
+      const bool ok = (vmask >> row) & 1u;
+      const size_t off = (base + lane_off[i]) * ESZ;
+      const void* ksrc = ok ? static_cast<const void*>(kpool + off) : &kZeroChunk;
+      const void* vsrc = ok ? static_cast<const void*>(vpool + off) : &kZeroChunk;
+      lds_dma16(ksrc, sb + i * 64);
+      lds_dma16(vsrc, sb + SBYTES / 16 + i * 64);
     }
     return vmask;
   };
@@ -547,15 +560,42 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_lds_kernel(D
   const uint2 ones = make_uint2(0x3F803F80u, 0x3F803F80u);
   const float c = a.scale_log2;
 
-  auto compute = [&](const StageBuf<D>* sb, uint32_t vmask) {
+  auto compute = [&](const uint4* sb, uint32_t vmask) {
+    const char* kr = reinterpret_cast<const char*>(sb);
+    const char* vr_in = kr + SBYTES;
     // ---- S^T = K Q^T --------------------------------------------------------
+    // A operand: key lq, head_dim elements 32*ks + 8*lg .. +8.
     floatx4_t s = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const int chunk = (4 * ks + lg) ^ (lq & SWZ);
-      const uint4 ka = *reinterpret_cast<const uint4*>(
-          reinterpret_cast<const char*>(sb->k) + lq * ROWB + chunk * 16);
+      uint4 ka;
+      if constexpr (KV8) {
+        const int chunk = (2 * ks + (lg >> 1)) ^ (lq & SWZ);
+        ka = widen_e4m3x8(*reinterpret_cast<const uint2*>(kr + lq * ROWB + chunk * 16 + 8 * (lg & 1)));
+      } else {
+        const int chunk = (4 * ks + lg) ^ (lq & SWZ);
+        ka = *reinterpret_cast<const uint4*>(kr + lq * ROWB + chunk * 16);
+      }
       s = mfma_k32(ka, qb[ks], s);
+    }
+    // FP8: widen the stage's V rows into this wave's bf16 tile (same row
+    // layout as the bf16 kernel reads). Only this wave touches the tile, and a
+    // wave's LDS accesses are performed in order.
+    const char* vr_bf = vr_in;
+    if constexpr (KV8) {
+      char* vw = reinterpret_cast<char*>(&vwide[wave][0]);
+#pragma unroll
+      for (int j = 0; j < CPT / 4; ++j) {
+        const int q = lane + 64 * j;  // fp8 chunk: row q / CPT, 16 elements (q % CPT)*16 ..
+        const int row = q / CPT;
+        const int cc = q % CPT;
+        const uint4 c8 = *reinterpret_cast<const uint4*>(vr_in + row * ROWB + ((cc ^ (row & SWZ)) << 4));
+        const uint4 lo = widen_e4m3x8(make_uint2(c8.x, c8.y));
+        const uint4 hi = widen_e4m3x8(make_uint2(c8.z, c8.w));
+        *reinterpret_cast<uint4*>(vw + row * VROWB + (((2 * cc) ^ (row & VSWZ)) << 4)) = lo;
+        *reinterpret_cast<uint4*>(vw + row * VROWB + (((2 * cc + 1) ^ (row & VSWZ)) << 4)) = hi;
+      }
+      vr_bf = vw;
     }
     // ---- mask (stages that straddle the range or hold an invalid block) ------
     if (vmask != 0xFFFFu) {
@@ -590,11 +630,11 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_lds_kernel(D
     // Lane (lq, lg) addresses key row 4*lg + lq/4, columns 16*nt + 4*(lq%4) .. +3;
     // the transposing read returns keys 4*lg .. 4*lg+3 of column 16*nt + lq.
     const int vrow = 4 * lg + (lq >> 2);
-    const char* vr = reinterpret_cast<const char*>(sb->v) + vrow * ROWB + 8 * (lq & 1);
+    const char* vr = vr_bf + vrow * VROWB + 8 * (lq & 1);
     lsum = mfma_k16(pa, ones, lsum);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const int chunk = (2 * nt + ((lq & 3) >> 1)) ^ (vrow & SWZ);
+      const int chunk = (2 * nt + ((lq & 3) >> 1)) ^ (vrow & VSWZ);
       const uint2 vb = ds_read_tr16(reinterpret_cast<const uint16_t*>(vr + chunk * 16));
       o[nt] = mfma_k16(pa, vb, o[nt]);
     }
@@ -608,8 +648,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_lds_kernel(D
   // The wave's stages are taken in windows whose blocks fit the 64-entry
   // table register; the pipeline drains at a window's end.
   constexpr int OPS = 2 * NI;  // load instructions per stage
-  StageBuf<D>* const slot0 = &ring0[wave];
-  StageBuf<D>* const slot1 = &ring1[wave];
+  uint4* const slot0 = &ring0[wave][0];
+  uint4* const slot1 = &ring1[wave][0];
   // Stages per window: an even count whose blocks (plus a block-size
   // misalignment of the first stage) stay within 64 table entries.
   const int spwin = ((63 << bs_log2) / kStageTokens) & ~1;
@@ -666,6 +706,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_lds_kernel(D
       A += sm_o[(w * 16 + g) * D + d] * f;
     }
     const size_t bh = static_cast<size_t>(b) * a.hq + h0 + g;
+    A *= a.v_scale;  // FP8: V codes stand for v_scale * value (1 for bf16: exact)
     if (a.out) {
       store_out<2>(a.out, bh * D + d, L > 0.f ? A / L : 0.f);
     } else {
@@ -793,9 +834,9 @@ int iter_tokens_f32(int d) {
 }
 
 // Query heads one workgroup handles: the largest supported size dividing the
-// group (bf16 kernel: up to 16, the MFMA row count; fp32 kernel: 4, 2, 1).
+// group (bf16 and FP8 kernel: up to 16, the MFMA row count; fp32 kernel: 4, 2, 1).
 int head_group_size(int group, int esz) {
-  if (esz == 2) {
+  if (esz <= 2) {
     for (int g = 16; g > 1; --g)
       if (group % g == 0) return g;
     return 1;
@@ -830,7 +871,7 @@ int32_t make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, int3
   const int32_t span = span_tokens(max_seq_len, window, block_size);
   const int64_t pairs = static_cast<int64_t>(batch) * hkv * (group / pl->gt);
   int32_t part = partition_tokens;
-  if (esz == 2) {
+  if (esz <= 2) {
     // Stage-streaming kernel: 16-token stages, four waves per workgroup
     // (two or more workgroups per CU, so one's start and merge overlap
     // another's streaming; eight waves in one workgroup measured slower).
@@ -897,17 +938,21 @@ void launch_partial_f32(const DecodeParams& prm, int gt, dim3 grid, dim3 block, 
 }
 
 template <int D>
-void launch_partial_bf16(const DecodeParams& prm, dim3 grid, dim3 block, hipStream_t s,
-                         const LaunchTrace& tr) {
-  hipExtLaunchKernelGGL(decode_partial_lds_kernel<D>, grid, block, 0, s, tr.start(), tr.stop(), 0, prm);
+void launch_partial_stage(const DecodeParams& prm, int kv_esz, dim3 grid, dim3 block,
+                          hipStream_t s, const LaunchTrace& tr) {
+  if (kv_esz == 1)
+    hipExtLaunchKernelGGL(decode_partial_lds_kernel<D, 1>, grid, block, 0, s, tr.start(), tr.stop(), 0, prm);
+  else
+    hipExtLaunchKernelGGL(decode_partial_lds_kernel<D, 2>, grid, block, 0, s, tr.start(), tr.stop(), 0, prm);
 }
 
-void launch_partial_any(const DecodeParams& prm, int esz, int d, int gt, dim3 grid, dim3 block,
+// kv_esz: bytes per pool element (4 fp32, 2 bf16, 1 FP8 codes with bf16 q/out).
+void launch_partial_any(const DecodeParams& prm, int kv_esz, int d, int gt, dim3 grid, dim3 block,
                         hipStream_t s, const LaunchTrace& tr) {
-  if (esz == 2) {
-    if (d == 64) launch_partial_bf16<64>(prm, grid, block, s, tr);
-    else if (d == 128) launch_partial_bf16<128>(prm, grid, block, s, tr);
-    else launch_partial_bf16<256>(prm, grid, block, s, tr);
+  if (kv_esz <= 2) {
+    if (d == 64) launch_partial_stage<64>(prm, kv_esz, grid, block, s, tr);
+    else if (d == 128) launch_partial_stage<128>(prm, kv_esz, grid, block, s, tr);
+    else launch_partial_stage<256>(prm, kv_esz, grid, block, s, tr);
   } else {
     if (d == 64) launch_partial_f32<64>(prm, gt, grid, block, s, tr);
     else if (d == 128) launch_partial_f32<128>(prm, gt, grid, block, s, tr);
@@ -963,17 +1008,18 @@ extern "C" int32_t paged_attn_decode_workspace_bytes(int32_t batch, int32_t num_
   return ok();
 }
 
-extern "C" int32_t paged_attn_decode(void* out, const void* q, const void* k_pool,
-                                     const void* v_pool, const int32_t* block_tables,
-                                     int32_t max_blocks_per_seq, const int32_t* seq_lens,
-                                     int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
-                                     int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                                     float scale, int32_t sliding_window,
-                                     int32_t partition_tokens, int32_t max_seq_len,
-                                     void* workspace, size_t workspace_bytes, int32_t dtype,
-                                     void* stream) {
-  const int esz = esize_of(dtype);
-  if (esz == 0) return fail(PAGED_ERR_DTYPE, "unknown dtype %d", dtype);
+namespace pagedkv {
+namespace {
+
+// Shared by the bf16/fp32 and the FP8 entry points. esz: pool element bytes
+// (q/out are bf16 when esz == 1).
+int32_t decode_impl(void* out, const void* q, const void* k_pool, const void* v_pool,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                    int32_t num_blocks, float scale, float k_scale, float v_scale,
+                    int32_t sliding_window, int32_t partition_tokens, int32_t max_seq_len,
+                    void* workspace, size_t workspace_bytes, int esz, void* stream) {
   Plan pl;
   if (int32_t rc = make_plan(batch, num_q_heads, num_kv_heads, head_dim, block_size, max_seq_len,
                              sliding_window, partition_tokens, esz, &pl))
@@ -981,6 +1027,8 @@ extern "C" int32_t paged_attn_decode(void* out, const void* q, const void* k_poo
   if (max_blocks_per_seq < 1 || num_blocks < 1)
     return fail(PAGED_ERR_INVALID_ARG, "max_blocks_per_seq and num_blocks must be positive");
   if (!std::isfinite(scale)) return fail(PAGED_ERR_INVALID_ARG, "scale must be finite");
+  if (!(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
+    return fail(PAGED_ERR_INVALID_ARG, "k_scale and v_scale must be finite and positive");
   if (batch > 65535 || num_q_heads > 65535)
     return fail(PAGED_ERR_INVALID_ARG, "batch and num_q_heads must be at most 65535");
   if (batch == 0) return ok();
@@ -1017,7 +1065,8 @@ extern "C" int32_t paged_attn_decode(void* out, const void* q, const void* k_poo
   prm.window = sliding_window;
   prm.part = pl.part;
   prm.max_parts = pl.max_parts;
-  prm.scale_log2 = scale * 1.4426950408889634f;
+  prm.scale_log2 = scale * 1.4426950408889634f * k_scale;
+  prm.v_scale = v_scale;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid(static_cast<unsigned>(pl.max_parts),
                   static_cast<unsigned>(num_kv_heads * prm.head_groups),
@@ -1033,10 +1082,46 @@ extern "C" int32_t paged_attn_decode(void* out, const void* q, const void* k_poo
     prm.out = out;
     const dim3 rgrid(static_cast<unsigned>((static_cast<int64_t>(batch) * num_q_heads + 3) / 4));
     LaunchTrace tr(PAGED_KERNEL_DECODE_REDUCE, s);
-    if (esz == 2) launch_reduce_d<2>(prm, head_dim, rgrid, s, tr);
+    if (esz <= 2) launch_reduce_d<2>(prm, head_dim, rgrid, s, tr);  // bf16 output
     else launch_reduce_d<4>(prm, head_dim, rgrid, s, tr);
     tr.finish();
     if (int32_t rc = check_launch("paged_attn_decode (reduce)")) return rc;
   }
   return ok();
+}
+
+}  // namespace
+}  // namespace pagedkv
+
+extern "C" int32_t paged_attn_decode(void* out, const void* q, const void* k_pool,
+                                     const void* v_pool, const int32_t* block_tables,
+                                     int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                     int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                     float scale, int32_t sliding_window,
+                                     int32_t partition_tokens, int32_t max_seq_len,
+                                     void* workspace, size_t workspace_bytes, int32_t dtype,
+                                     void* stream) {
+  if (dtype != PAGED_F32 && dtype != PAGED_BF16)
+    return fail(PAGED_ERR_DTYPE, "paged_attn_decode takes f32 or bf16 (FP8 pools: paged_attn_decode_fp8), got %d",
+                dtype);
+  return decode_impl(out, q, k_pool, v_pool, block_tables, max_blocks_per_seq, seq_lens, batch,
+                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, 1.f, 1.f,
+                     sliding_window, partition_tokens, max_seq_len, workspace, workspace_bytes,
+                     esize_of(dtype), stream);
+}
+
+extern "C" int32_t paged_attn_decode_fp8(void* out, const void* q, const void* k_pool,
+                                         const void* v_pool, const int32_t* block_tables,
+                                         int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                         int32_t batch, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim,
+                                         int32_t block_size, int32_t num_blocks, float scale,
+                                         float k_scale, float v_scale, int32_t sliding_window,
+                                         int32_t partition_tokens, int32_t max_seq_len,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(out, q, k_pool, v_pool, block_tables, max_blocks_per_seq, seq_lens, batch,
+                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, k_scale,
+                     v_scale, sliding_window, partition_tokens, max_seq_len, workspace,
+                     workspace_bytes, 1, stream);
 }

@@ -87,4 +87,15 @@ __device__ __forceinline__ float max_across_groups(float x) {
   return fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
 }
 
+// Eight E4M3 codes (bytes of v, low first) to eight bf16 values, exactly:
+// every E4M3 value is a bf16 value.
+__device__ __forceinline__ uint4 widen_e4m3x8(const uint2& v) {
+  const auto f0 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(v.x), false);
+  const auto f1 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(v.x), true);
+  const auto f2 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(v.y), false);
+  const auto f3 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(v.y), true);
+  return make_uint4(pack_bf16x2(f0[0], f0[1]), pack_bf16x2(f1[0], f1[1]),
+                    pack_bf16x2(f2[0], f2[1]), pack_bf16x2(f3[0], f3[1]));
+}
+
 }  // namespace pagedkv

@@ -43,8 +43,8 @@ typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
 struct PrefillParams {
   uint16_t* out;
   const uint16_t* q;
-  const uint16_t* k_pool;
-  const uint16_t* v_pool;
+  const void* k_pool;       // bf16 values or FP8 E4M3 codes
+  const void* v_pool;
   const int32_t* bt;
   const int32_t* cu_q;
   const int32_t* seq_lens;
@@ -52,7 +52,8 @@ struct PrefillParams {
   int32_t tiles_per_head;   // ceil(max_q_len * group / kTileM)
   int32_t work_items;       // batch * hkv * tiles_per_head
   int32_t per_xcd;          // ceil(work_items / kNumXcd)
-  float scale_log2;
+  float scale_log2;         // scale * log2(e) (times the K scale for FP8 pools)
+  float v_scale;            // FP8 pools: the V scale; 1 otherwise
 };
 
 __device__ __forceinline__ floatx4_t mfma16x16x32(const uint4& a, const uint4& b, floatx4_t c) {
@@ -60,7 +61,9 @@ __device__ __forceinline__ floatx4_t mfma16x16x32(const uint4& a, const uint4& b
                                                  __builtin_bit_cast(bf16x8v, b), c, 0, 0, 0);
 }
 
-template <int D>
+// ESZ: bytes per pool element (2: bf16; 1: FP8 E4M3 codes, widened to bf16
+// exactly as they are staged, so everything after staging is shared).
+template <int D, int ESZ>
 __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillParams a) {
   // LDS row strides (elements): rows padded by 32 bytes. Measured on gfx950
   // with the two read patterns below (K: 16 rows x 64 bytes per ds_read_b128;
@@ -171,6 +174,14 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillParams a
 #pragma unroll
   for (int i = 0; i < KI; ++i)
     lane_off[i] = static_cast<uint32_t>(((lane / DCH + KROWS * i) & (bs8 ? 7 : 15)) * D + k_dc * 8);
+  // Eight head_dim elements of one key row as bf16 (16 bytes): read as they
+  // are (bf16) or widened from eight E4M3 codes.
+  auto load_row_chunk = [&](const void* pool, size_t elem) -> uint4 {
+    if constexpr (ESZ == 1)
+      return widen_e4m3x8(*reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(pool) + elem));
+    else
+      return *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(pool) + elem);
+  };
   auto stage_load = [&](int kt, int ent) {
     const int ts = kt * kTileN;
     const int e0 = (wave * 16) >> bs_log2;
@@ -185,8 +196,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillParams a
 #pragma unroll
       for (int i = 0; i < KI; ++i) {
         const size_t base = (bs8 && KROWS * i >= 8) ? base_hi : base_lo;
-        kreg[i] = *reinterpret_cast<const uint4*>(a.k_pool + base + lane_off[i]);
-        vreg[i] = *reinterpret_cast<const uint4*>(a.v_pool + base + lane_off[i]);
+        kreg[i] = load_row_chunk(a.k_pool, base + lane_off[i]);
+        vreg[i] = load_row_chunk(a.v_pool, base + lane_off[i]);
       }
     } else {
 #pragma unroll
@@ -195,8 +206,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillParams a
         const int phys = hi ? phys_hi : phys_lo;
         const size_t base = hi ? base_hi : base_lo;
         if (ts + k_key + KROWS * i < n && phys_ok(phys)) {
-          kreg[i] = *reinterpret_cast<const uint4*>(a.k_pool + base + lane_off[i]);
-          vreg[i] = *reinterpret_cast<const uint4*>(a.v_pool + base + lane_off[i]);
+          kreg[i] = load_row_chunk(a.k_pool, base + lane_off[i]);
+          vreg[i] = load_row_chunk(a.v_pool, base + lane_off[i]);
         } else {
           kreg[i] = make_uint4(0, 0, 0, 0);
           vreg[i] = make_uint4(0, 0, 0, 0);
@@ -353,7 +364,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillParams a
   for (int j = 0; j < 2; ++j) {
     float inv[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) inv[i] = lsum[j][i] > 0.f ? 1.f / lsum[j][i] : 0.f;
+    for (int i = 0; i < 4; ++i) inv[i] = lsum[j][i] > 0.f ? a.v_scale / lsum[j][i] : 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = r_first + wave * kRowsPerWave + 16 * j + 4 * lg + i;
@@ -373,16 +384,17 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillParams a
 
 using namespace pagedkv;
 
-extern "C" int32_t paged_attn_prefill_chunk(void* out, const void* q, const void* k_pool,
-                                            const void* v_pool, const int32_t* block_tables,
-                                            int32_t max_blocks_per_seq, const int32_t* cu_q_lens,
-                                            const int32_t* seq_lens, int32_t batch,
-                                            int32_t total_q, int32_t max_q_len,
-                                            int32_t num_q_heads, int32_t num_kv_heads,
-                                            int32_t head_dim, int32_t block_size,
-                                            int32_t num_blocks, float scale,
-                                            int32_t sliding_window, int32_t dtype, void* stream) {
-  if (dtype != PAGED_BF16) return fail(PAGED_ERR_DTYPE, "prefill supports bf16 only");
+namespace pagedkv {
+namespace {
+
+// Shared by the bf16 and FP8 entry points; esz: pool element bytes (q/out bf16).
+int32_t prefill_impl(void* out, const void* q, const void* k_pool, const void* v_pool,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* cu_q_lens, const int32_t* seq_lens, int32_t batch,
+                     int32_t total_q, int32_t max_q_len, int32_t num_q_heads,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                     int32_t num_blocks, float scale, float k_scale, float v_scale,
+                     int32_t sliding_window, int esz, void* stream) {
   if (head_dim != 64 && head_dim != 128 && head_dim != 256)
     return fail(PAGED_ERR_INVALID_ARG, "head_dim must be 64, 128 or 256 (got %d)", head_dim);
   if (!pow2_in(block_size, 8, 64))
@@ -394,6 +406,8 @@ extern "C" int32_t paged_attn_prefill_chunk(void* out, const void* q, const void
     return fail(PAGED_ERR_INVALID_ARG, "bad size argument");
   if (!std::isfinite(scale) || scale < 0.f)
     return fail(PAGED_ERR_INVALID_ARG, "scale must be finite and non-negative");
+  if (!(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
+    return fail(PAGED_ERR_INVALID_ARG, "k_scale and v_scale must be finite and positive");
   if (batch == 0 || total_q == 0 || max_q_len == 0) return ok();
   if (!out || !q || !k_pool || !v_pool || !block_tables || !cu_q_lens || !seq_lens)
     return fail(PAGED_ERR_INVALID_ARG, "NULL pointer");
@@ -406,8 +420,8 @@ extern "C" int32_t paged_attn_prefill_chunk(void* out, const void* q, const void
   PrefillParams prm{};
   prm.out = static_cast<uint16_t*>(out);
   prm.q = static_cast<const uint16_t*>(q);
-  prm.k_pool = static_cast<const uint16_t*>(k_pool);
-  prm.v_pool = static_cast<const uint16_t*>(v_pool);
+  prm.k_pool = k_pool;
+  prm.v_pool = v_pool;
   prm.bt = block_tables;
   prm.cu_q = cu_q_lens;
   prm.seq_lens = seq_lens;
@@ -421,17 +435,61 @@ extern "C" int32_t paged_attn_prefill_chunk(void* out, const void* q, const void
   prm.tiles_per_head = static_cast<int32_t>(tiles);
   prm.work_items = static_cast<int32_t>(items);
   prm.per_xcd = static_cast<int32_t>((items + kNumXcd - 1) / kNumXcd);
-  prm.scale_log2 = scale * 1.4426950408889634f;
+  prm.scale_log2 = scale * 1.4426950408889634f * k_scale;
+  prm.v_scale = v_scale;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid(static_cast<unsigned>(prm.per_xcd * kNumXcd));
   const dim3 block(kWaves * 64);
   LaunchTrace tr(PAGED_KERNEL_PREFILL, s);
-  if (head_dim == 64)
-    hipExtLaunchKernelGGL(prefill_kernel<64>, grid, block, 0, s, tr.start(), tr.stop(), 0, prm);
-  else if (head_dim == 128)
-    hipExtLaunchKernelGGL(prefill_kernel<128>, grid, block, 0, s, tr.start(), tr.stop(), 0, prm);
-  else
-    hipExtLaunchKernelGGL(prefill_kernel<256>, grid, block, 0, s, tr.start(), tr.stop(), 0, prm);
+  if (esz == 1) {
+    if (head_dim == 64)
+      hipExtLaunchKernelGGL(prefill_kernel<64, 1>, grid, block, 0, s, tr.start(), tr.stop(), 0, prm);
+    else if (head_dim == 128)
+      hipExtLaunchKernelGGL(prefill_kernel<128, 1>, grid, block, 0, s, tr.start(), tr.stop(), 0, prm);
+    else
+      hipExtLaunchKernelGGL(prefill_kernel<256, 1>, grid, block, 0, s, tr.start(), tr.stop(), 0, prm);
+  } else {
+    if (head_dim == 64)
+      hipExtLaunchKernelGGL(prefill_kernel<64, 2>, grid, block, 0, s, tr.start(), tr.stop(), 0, prm);
+    else if (head_dim == 128)
+      hipExtLaunchKernelGGL(prefill_kernel<128, 2>, grid, block, 0, s, tr.start(), tr.stop(), 0, prm);
+    else
+      hipExtLaunchKernelGGL(prefill_kernel<256, 2>, grid, block, 0, s, tr.start(), tr.stop(), 0, prm);
+  }
   tr.finish();
   return check_launch("paged_attn_prefill_chunk");
+}
+
+}  // namespace
+}  // namespace pagedkv
+
+extern "C" int32_t paged_attn_prefill_chunk(void* out, const void* q, const void* k_pool,
+                                            const void* v_pool, const int32_t* block_tables,
+                                            int32_t max_blocks_per_seq, const int32_t* cu_q_lens,
+                                            const int32_t* seq_lens, int32_t batch,
+                                            int32_t total_q, int32_t max_q_len,
+                                            int32_t num_q_heads, int32_t num_kv_heads,
+                                            int32_t head_dim, int32_t block_size,
+                                            int32_t num_blocks, float scale,
+                                            int32_t sliding_window, int32_t dtype, void* stream) {
+  if (dtype != PAGED_BF16)
+    return fail(PAGED_ERR_DTYPE, "prefill takes bf16 (FP8 pools: paged_attn_prefill_chunk_fp8)");
+  return prefill_impl(out, q, k_pool, v_pool, block_tables, max_blocks_per_seq, cu_q_lens,
+                      seq_lens, batch, total_q, max_q_len, num_q_heads, num_kv_heads, head_dim,
+                      block_size, num_blocks, scale, 1.f, 1.f, sliding_window, 2, stream);
+}
+
+extern "C" int32_t paged_attn_prefill_chunk_fp8(void* out, const void* q, const void* k_pool,
+                                                const void* v_pool, const int32_t* block_tables,
+                                                int32_t max_blocks_per_seq,
+                                                const int32_t* cu_q_lens, const int32_t* seq_lens,
+                                                int32_t batch, int32_t total_q, int32_t max_q_len,
+                                                int32_t num_q_heads, int32_t num_kv_heads,
+                                                int32_t head_dim, int32_t block_size,
+                                                int32_t num_blocks, float scale, float k_scale,
+                                                float v_scale, int32_t sliding_window,
+                                                void* stream) {
+  return prefill_impl(out, q, k_pool, v_pool, block_tables, max_blocks_per_seq, cu_q_lens,
+                      seq_lens, batch, total_q, max_q_len, num_q_heads, num_kv_heads, head_dim,
+                      block_size, num_blocks, scale, k_scale, v_scale, sliding_window, 1, stream);
 }

@@ -31,7 +31,9 @@ class LaunchTrace {
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-inline int esize_of(int32_t dtype) { return dtype == PAGED_BF16 ? 2 : dtype == PAGED_F32 ? 4 : 0; }
+inline int esize_of(int32_t dtype) {
+  return dtype == PAGED_BF16 ? 2 : dtype == PAGED_F32 ? 4 : dtype == PAGED_FP8_E4M3 ? 1 : 0;
+}
 
 inline bool pow2_in(int32_t x, int32_t lo, int32_t hi) {
   return x >= lo && x <= hi && (x & (x - 1)) == 0;

@@ -68,7 +68,11 @@ enum {
   PAGED_ERR_HIP = -6          /* HIP runtime error (launch, device query) */
 };
 
-enum { PAGED_F32 = 0, PAGED_BF16 = 1 };
+/* Element types. PAGED_FP8_E4M3 is the FP8 KV-cache format (perf doc,
+ * quantization table: FP8 KV cache row, per-layer scales): OCP E4M3 codes
+ * (bias 7, max 448, 0x7F/0xFF NaN); a stored code c stands for scale * c with
+ * one K scale and one V scale per layer pool. */
+enum { PAGED_F32 = 0, PAGED_BF16 = 1, PAGED_FP8_E4M3 = 2 };
 
 /* Returns PAGEDKV_ABI_VERSION. */
 int32_t paged_abi_version(void);
@@ -82,7 +86,9 @@ const char* paged_last_error(void);
  * -------------------------------------------------------------------- */
 
 /* Slot-mapped KV write (perf doc, paged-attention knobs table: native paged
- * K/V write). For every t in [0, num_tokens) with
+ * K/V write); dtype PAGED_F32, PAGED_BF16, or PAGED_FP8_E4M3 to copy codes
+ * that are already quantized (paged_kv_write_fp8 quantizes). For every t in
+ * [0, num_tokens) with
  * 0 <= slot_mapping[t] < num_blocks * block_size:
  *   k_pool[slot / block_size][h][slot % block_size][:] = new_k[t][h][:]
  * for every KV head h, and the same for V. Tokens with a negative or
@@ -97,6 +103,21 @@ int32_t paged_kv_write(void* k_pool, void* v_pool, const void* new_k, const void
                        int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
                        int32_t dtype, void* stream);
 
+/* Quantizing KV write into FP8 pools (perf doc, quantization table: FP8 KV
+ * cache with per-layer scales). As paged_kv_write, but each element x of
+ * new_k (new_v) is stored as the E4M3 code of x / k_scale (x / v_scale):
+ * the division in float32 (correctly rounded), then the nearest E4M3 value
+ * with ties to the even code, magnitudes above 448 saturated to 448.
+ *   k_pool, v_pool : device, uint8 codes [num_blocks][num_kv_heads][block_size][head_dim]
+ *   new_k, new_v   : device, src_dtype (PAGED_BF16 or PAGED_F32),
+ *                    [num_tokens][num_kv_heads][head_dim], finite
+ *   k_scale, v_scale : finite, > 0
+ * Errors as paged_kv_write; PAGED_ERR_DTYPE for another src_dtype. */
+int32_t paged_kv_write_fp8(void* k_pool, void* v_pool, const void* new_k, const void* new_v,
+                           const int64_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                           int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t src_dtype, float k_scale, float v_scale, void* stream);
+
 /* Gather the attended positions of each row into contiguous buffers (perf doc,
  * paged-attention knobs table: the synchronous decode gather reads the pages a
  * row attends to, sliding groups from their first live block). A diagnostic
@@ -107,7 +128,9 @@ int32_t paged_kv_write(void* k_pool, void* v_pool, const void* new_k, const void
  *   block_tables : device, int32 [batch][max_blocks_per_seq]
  *   seq_lens     : device, int32 [batch], each in [0, max_seq_len]
  *   out_offsets  : device, int64 [batch] (row start in out, in tokens)
- *   out_k, out_v : device, [sum of spans][num_kv_heads][head_dim] */
+ *   out_k, out_v : device, [sum of spans][num_kv_heads][head_dim]
+ * Elements are copied as bytes: dtype PAGED_F32, PAGED_BF16 or PAGED_FP8_E4M3
+ * (codes). */
 int32_t paged_kv_gather(void* out_k, void* out_v, const void* k_pool, const void* v_pool,
                         const int32_t* block_tables, int32_t max_blocks_per_seq,
                         const int32_t* seq_lens, const int64_t* out_offsets, int32_t batch,
@@ -168,6 +191,19 @@ int32_t paged_attn_decode(void* out, const void* q, const void* k_pool, const vo
                           int32_t partition_tokens, int32_t max_seq_len, void* workspace,
                           size_t workspace_bytes, int32_t dtype, void* stream);
 
+/* paged_attn_decode over FP8 pools: K[t] = k_scale * E4M3(k code), V[t] =
+ * v_scale * E4M3(v code); q and out bf16. Same partitions, workspace (query
+ * it with dtype PAGED_FP8_E4M3) and errors as paged_attn_decode.
+ *   k_scale, v_scale : finite, > 0, the scales the pools were written with */
+int32_t paged_attn_decode_fp8(void* out, const void* q, const void* k_pool, const void* v_pool,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                              const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              int32_t num_blocks, float scale, float k_scale, float v_scale,
+                              int32_t sliding_window, int32_t partition_tokens,
+                              int32_t max_seq_len, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
 /* Chunked-prefill attention over a cached paged prefix (perf doc, knobs table:
  * prefill chunk size; the paged-attention bridge for prefill over a cache hit
  * that reads K/V through the pages). Row b owns query rows
@@ -191,6 +227,17 @@ int32_t paged_attn_prefill_chunk(void* out, const void* q, const void* k_pool,
                                  int32_t head_dim, int32_t block_size, int32_t num_blocks,
                                  float scale, int32_t sliding_window, int32_t dtype,
                                  void* stream);
+
+/* paged_attn_prefill_chunk over FP8 pools (K, V as in paged_attn_decode_fp8);
+ * q and out bf16. Same arguments and errors otherwise. */
+int32_t paged_attn_prefill_chunk_fp8(void* out, const void* q, const void* k_pool,
+                                     const void* v_pool, const int32_t* block_tables,
+                                     int32_t max_blocks_per_seq, const int32_t* cu_q_lens,
+                                     const int32_t* seq_lens, int32_t batch, int32_t total_q,
+                                     int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                     float scale, float k_scale, float v_scale,
+                                     int32_t sliding_window, void* stream);
 
 /* ----------------------------------------------------------------------
  * Kernel timing (HIP events around every launch, on the launch's stream)

@@ -38,27 +38,36 @@ def torch_dtype(wl):
 
 
 def gpu_setup(wl, tabs, fill=float("nan"), device="cuda"):
-    """Device pools with the cached context written; returns per-layer dicts."""
+    """Device pools with the cached context written; returns per-layer dicts.
+
+    FP8 workloads get float8_e4m3fn pools (the fill becomes its code: NaN is
+    0x7F) written by the quantizing write with the layer's scales."""
     import torch
 
     import block_paged_kv_amd as pk
 
     dt = torch_dtype(wl)
+    fp8 = wl.kv_dtype == "fp8"
+    pool_dt = torch.float8_e4m3fn if fp8 else dt
     dev = {}
     for L in wl.layers:
         if L.alias_of:
             continue
         shape = (L.num_blocks, wl.hkv, wl.block_size, wl.head_dim)
-        kp = torch.full(shape, fill, dtype=dt, device=device)
-        vp = torch.full(shape, fill, dtype=dt, device=device)
+        kp = torch.full(shape, fill, dtype=pool_dt, device=device)
+        vp = torch.full(shape, fill, dtype=pool_dt, device=device)
         t = tabs[L.name]
         sk, sv = synth.setup_kv(wl, L)
         slots = np.concatenate(t["setup_slots"]) if t["setup_slots"] else np.zeros(0, np.int64)
         say(f"[gpu] setup write {wl.name}/{L.name}: {slots.shape[0]} tokens")
         if slots.shape[0]:
-            pk.paged_kv_write(kp, vp, torch.from_numpy(sk).to(device=device, dtype=dt),
-                              torch.from_numpy(sv).to(device=device, dtype=dt),
-                              torch.from_numpy(slots).to(device))
+            ksrc = torch.from_numpy(sk).to(device=device, dtype=dt)
+            vsrc = torch.from_numpy(sv).to(device=device, dtype=dt)
+            sl = torch.from_numpy(slots).to(device)
+            if fp8:
+                pk.paged_kv_write_fp8(kp, vp, ksrc, vsrc, sl, L.k_scale, L.v_scale)
+            else:
+                pk.paged_kv_write(kp, vp, ksrc, vsrc, sl)
         stk, stv = synth.step_kv(wl, L)
         dev[L.name] = dict(
             k_pool=kp, v_pool=vp,
@@ -72,6 +81,8 @@ def gpu_setup(wl, tabs, fill=float("nan"), device="cuda"):
             dev[L.name] = dict(dev[L.alias_of])
         dev[L.name]["q"] = torch.from_numpy(L.q).to(device=device, dtype=dt)
         dev[L.name]["window"] = L.window
+        dev[L.name]["k_scale"] = L.k_scale
+        dev[L.name]["v_scale"] = L.v_scale
     dev["_seq_lens"] = torch.from_numpy(wl.seq_lens.astype(np.int32)).to(device)
     if wl.kind == "prefill":
         cu = np.concatenate([[0], np.cumsum(wl.chunk_lens)]).astype(np.int32)
@@ -89,8 +100,9 @@ def gpu_workspace(wl, dev, partition_tokens=None, max_seq_len=None):
         return None
     part = wl.partition_tokens if partition_tokens is None else partition_tokens
     msl = wl.max_seq_len if max_seq_len is None else max_seq_len
+    dt = "fp8" if wl.kv_dtype == "fp8" else wl.dtype
     need = max(pk.paged_attn_decode_workspace_bytes(wl.batch, wl.hq, wl.hkv, wl.head_dim,
-                                                    wl.block_size, msl, L.window, part, wl.dtype)
+                                                    wl.block_size, msl, L.window, part, dt)
                for L in wl.layers)
     return torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
 
@@ -105,19 +117,35 @@ def gpu_step(wl, dev, outs=None, workspace=None, partition_tokens=None, max_seq_
     names = [L.name for L in wl.layers] if layers is None else layers
     if outs is None:
         outs = {n: torch.empty_like(dev[n]["q"]) for n in names}
+    fp8 = wl.kv_dtype == "fp8"
     for L in wl.layers:
         if L.alias_of or L.name not in names:
             continue
         d = dev[L.name]
-        pk.paged_kv_write(d["k_pool"], d["v_pool"], d["step_k"], d["step_v"], d["step_slots"])
+        if fp8:
+            pk.paged_kv_write_fp8(d["k_pool"], d["v_pool"], d["step_k"], d["step_v"], d["step_slots"],
+                                  d["k_scale"], d["v_scale"])
+        else:
+            pk.paged_kv_write(d["k_pool"], d["v_pool"], d["step_k"], d["step_v"], d["step_slots"])
     part = wl.partition_tokens if partition_tokens is None else partition_tokens
     msl = wl.max_seq_len if max_seq_len is None else max_seq_len
     for n in names:
         d = dev[n]
         if wl.kind == "decode":
-            pk.paged_attn_decode(outs[n], d["q"], d["k_pool"], d["v_pool"], d["tables"],
-                                 dev["_seq_lens"], wl.scale, msl, sliding_window=d["window"],
-                                 partition_tokens=part, workspace=workspace)
+            if fp8:
+                pk.paged_attn_decode_fp8(outs[n], d["q"], d["k_pool"], d["v_pool"], d["tables"],
+                                         dev["_seq_lens"], wl.scale, d["k_scale"], d["v_scale"], msl,
+                                         sliding_window=d["window"], partition_tokens=part,
+                                         workspace=workspace)
+            else:
+                pk.paged_attn_decode(outs[n], d["q"], d["k_pool"], d["v_pool"], d["tables"],
+                                     dev["_seq_lens"], wl.scale, msl, sliding_window=d["window"],
+                                     partition_tokens=part, workspace=workspace)
+        elif fp8:
+            pk.paged_attn_prefill_chunk_fp8(outs[n], d["q"], d["k_pool"], d["v_pool"], d["tables"],
+                                            dev["_cu_q"], dev["_seq_lens"], int(wl.chunk_lens.max()),
+                                            wl.scale, d["k_scale"], d["v_scale"],
+                                            sliding_window=d["window"])
         else:
             pk.paged_attn_prefill_chunk(outs[n], d["q"], d["k_pool"], d["v_pool"], d["tables"],
                                         dev["_cu_q"], dev["_seq_lens"], int(wl.chunk_lens.max()),
@@ -127,22 +155,39 @@ def gpu_step(wl, dev, outs=None, workspace=None, partition_tokens=None, max_seq_
 
 # ====================================================================== oracle
 def oracle_setup(wl, tabs_ref):
-    """float32 pools (NaN canaries elsewhere) holding the same tokens as the GPU pools."""
+    """float32 pools (NaN canaries elsewhere) holding the same tokens as the GPU pools.
+
+    FP8 workloads: the oracle quantizes the same inputs into uint8 code pools
+    (canary code 0x7F, NaN); ``pools["_codes"][layer]`` keeps them for the
+    bit-exact write check, and the attention pools hold their dequantized
+    values (scale * E4M3 value, float64)."""
     import oracle
 
     pools = {}
+    fp8 = wl.kv_dtype == "fp8"
+    if fp8:
+        pools["_codes"] = {}
     for L in wl.layers:
         if L.alias_of:
             continue
         shape = (L.num_blocks, wl.hkv, wl.block_size, wl.head_dim)
-        kp = np.full(shape, np.nan, dtype=np.float32)
-        vp = np.full(shape, np.nan, dtype=np.float32)
         t = tabs_ref[L.name]
         sk, sv = synth.setup_kv(wl, L)
         stk, stv = synth.step_kv(wl, L)
         slots = np.concatenate(t["setup_slots"] + t["step_slots"])
-        kp, vp = oracle.kv_write(kp, vp, np.concatenate([sk, stk]), np.concatenate([sv, stv]), slots,
-                                 wl.block_size)
+        new_k, new_v = np.concatenate([sk, stk]), np.concatenate([sv, stv])
+        if fp8:
+            kc = np.full(shape, 0x7F, dtype=np.uint8)
+            vc = np.full(shape, 0x7F, dtype=np.uint8)
+            kc, vc = oracle.kv_write(kc, vc, oracle.fp8.quantize(new_k, L.k_scale),
+                                     oracle.fp8.quantize(new_v, L.v_scale), slots, wl.block_size)
+            pools["_codes"][L.name] = (kc, vc)
+            kp = oracle.fp8.dequantize(kc, L.k_scale)
+            vp = oracle.fp8.dequantize(vc, L.v_scale)
+        else:
+            kp = np.full(shape, np.nan, dtype=np.float32)
+            vp = np.full(shape, np.nan, dtype=np.float32)
+            kp, vp = oracle.kv_write(kp, vp, new_k, new_v, slots, wl.block_size)
         pools[L.name] = (kp, vp, t["tables"])
     for L in wl.layers:
         if L.alias_of:

@@ -61,6 +61,8 @@ class Layer:
     v: list = field(default_factory=list)
     live_from: list = field(default_factory=list)  # per row: first position with data
     q: np.ndarray | None = None          # decode [B, Hq, D]; prefill [T, Hq, D]
+    k_scale: float = 1.0                 # FP8 pools: per-layer scales (float32 values)
+    v_scale: float = 1.0
 
 
 @dataclass
@@ -81,6 +83,7 @@ class Workload:
     block_size: int = BLOCK_SIZE
     domain: int = 0
     wave_size: int = 0        # rows per benchmark step when several batches share a pool
+    kv_dtype: str = ""        # "" = the pools hold ``dtype``; "fp8" = E4M3 codes with per-layer scales
 
     @property
     def max_seq_len(self):
@@ -112,14 +115,41 @@ def _suffix_tokens(b, length):
 
 def make(name, *, batch=None, hq=None, hkv=None, head_dim=None, context=None, prefix=None,
          num_blocks=None, seed=None, chunk=None, window=None, dtype=None, part=None,
-         num_prefixes=None, sliding_blocks=None, waves=None, block_size=None):
+         num_prefixes=None, sliding_blocks=None, waves=None, block_size=None, kv_dtype=None):
     """Build workload ``name`` at its published sizes; keyword overrides shrink it for tests.
 
     ``block_size`` (a power of two in [8, 64], default 16) changes only the paging:
-    the random draws are the same, prefix lengths round to whole blocks."""
+    the random draws are the same, prefix lengths round to whole blocks.
+    ``kv_dtype="fp8"`` (bf16 workloads) stores the pools as FP8 E4M3 codes with a
+    K and a V scale per layer: max |x| of the layer's K (V) over 448, so nothing
+    saturates; the draws are the same."""
     bs = BLOCK_SIZE if block_size is None else int(block_size)
     seed = SEEDS[name] if seed is None else seed
     rng = np.random.default_rng(seed)
+    wl = _make(name, rng, bs, batch=batch, hq=hq, hkv=hkv, head_dim=head_dim, context=context,
+               prefix=prefix, num_blocks=num_blocks, chunk=chunk, window=window, dtype=dtype,
+               part=part, num_prefixes=num_prefixes, sliding_blocks=sliding_blocks, waves=waves)
+    if kv_dtype:
+        if kv_dtype != "fp8" or wl.dtype != "bf16":
+            raise ValueError("kv_dtype='fp8' needs a bf16 workload")
+        wl.kv_dtype = "fp8"
+        for L in wl.layers:
+            if L.alias_of:
+                continue
+            kmax = max(float(np.abs(x).max()) if x.size else 0.0 for x in L.k)
+            vmax = max(float(np.abs(x).max()) if x.size else 0.0 for x in L.v)
+            L.k_scale = float(np.float32(max(kmax, 1e-6) / 448.0))
+            L.v_scale = float(np.float32(max(vmax, 1e-6) / 448.0))
+        for L in wl.layers:
+            if L.alias_of:
+                A = wl.layer(L.alias_of)
+                L.k_scale, L.v_scale = A.k_scale, A.v_scale
+    return wl
+
+
+def _make(name, rng, bs, *, batch=None, hq=None, hkv=None, head_dim=None, context=None, prefix=None,
+          num_blocks=None, chunk=None, window=None, dtype=None, part=None, num_prefixes=None,
+          sliding_blocks=None, waves=None):
 
     if name == "tiny":
         B, Hq, Hkv, D = batch or 2, hq or 4, hkv or 2, head_dim or 64
