@@ -18,7 +18,12 @@ the dominant kernel (its average launch time from HIP events recorded by the
 library on the launch stream over the timed region) and the CPU oracle's rate
 on a bounded sample of the same workload.
 
-    python bench.py [--workload qwen3|mixed|hybrid|prefill|tiny] [--steps K] [--warmup W]
+    python bench.py [--workload qwen3|mixed|hybrid|prefill|tiny] [--kv bf16|fp8]
+                    [--steps K] [--warmup W]
+
+``--kv fp8`` runs the same workload over FP8 (E4M3) pools with per-layer
+scales (quantizing write, FP8 decode/prefill); the decode byte count then
+counts one byte per K/V element.
 """
 
 from __future__ import annotations
@@ -50,6 +55,7 @@ def decode_bytes(wl, tabs, rows):
     distinct live K/V token rows (shared prefix blocks once) + Q + O + the
     block-table entries the rows attend through."""
     esz = 2 if wl.dtype == "bf16" else 4
+    kv_esz = 1 if wl.kv_dtype == "fp8" else esz
     total = 0
     for L in wl.layers:
         src = L.alias_of or L.name
@@ -62,7 +68,7 @@ def decode_bytes(wl, tabs, rows):
             for p in range(lo, n):
                 seen.add((int(t[b][p // wl.block_size]), p % wl.block_size))
             nblk += -(-n // wl.block_size) - lo // wl.block_size
-        kv = len(seen) * wl.hkv * wl.head_dim * esz * 2
+        kv = len(seen) * wl.hkv * wl.head_dim * kv_esz * 2
         qo = 2 * len(rows) * wl.hq * wl.head_dim * esz
         total += kv + qo + 4 * nblk
     return total
@@ -217,6 +223,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qwen3", choices=["qwen3", "mixed", "hybrid", "prefill", "tiny"])
     ap.add_argument("--waves", type=int, default=None, help="independent batches rotated through")
+    ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"], help="KV pool element type")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
@@ -241,6 +248,12 @@ def main():
     steps = args.steps or DEFAULT_STEPS[args.workload]
     waves = args.waves or DEFAULT_WAVES.get(args.workload, 1)
     kw = {"waves": waves} if args.workload == "qwen3" else {}
+    if args.kv == "fp8":
+        if args.workload == "tiny":
+            print("bench.py: --kv fp8 needs a bf16 workload (not tiny)", file=sys.stderr)
+            sys.exit(2)
+        kw["kv_dtype"] = "fp8"
+    fp8 = args.kv == "fp8"
     log(f"[bench] building workload {args.workload} ({kw})")
     wl = synth.make(args.workload, **kw)
     R = waves if args.workload == "qwen3" else 1
@@ -270,16 +283,33 @@ def main():
             nt = wl.new_tokens
             t0 = sum(nt[:r * wsz])
             t1 = sum(nt[:(r + 1) * wsz])
-            seq.append(pk.paged_kv_write(d["k_pool"], d["v_pool"], d["step_k"][t0:t1], d["step_v"][t0:t1],
-                                         d["step_slots"][t0:t1], stream=stream, prepare=True))
+            if fp8:
+                seq.append(pk.paged_kv_write_fp8(d["k_pool"], d["v_pool"], d["step_k"][t0:t1],
+                                                 d["step_v"][t0:t1], d["step_slots"][t0:t1], L.k_scale,
+                                                 L.v_scale, stream=stream, prepare=True))
+            else:
+                seq.append(pk.paged_kv_write(d["k_pool"], d["v_pool"], d["step_k"][t0:t1],
+                                             d["step_v"][t0:t1], d["step_slots"][t0:t1], stream=stream,
+                                             prepare=True))
         for L in wl.layers:
             d = dev[L.name]
-            if wl.kind == "decode":
+            if wl.kind == "decode" and fp8:
+                seq.append(pk.paged_attn_decode_fp8(
+                    outs[L.name], d["q"][rows], d["k_pool"], d["v_pool"], d["tables"][rows],
+                    dev["_seq_lens"][rows], wl.scale, L.k_scale, L.v_scale, int(wl.seq_lens[rows].max()),
+                    sliding_window=L.window, partition_tokens=wl.partition_tokens, workspace=ws,
+                    stream=stream, prepare=True))
+            elif wl.kind == "decode":
                 seq.append(pk.paged_attn_decode(
                     outs[L.name], d["q"][rows], d["k_pool"], d["v_pool"], d["tables"][rows],
                     dev["_seq_lens"][rows], wl.scale, int(wl.seq_lens[rows].max()),
                     sliding_window=L.window, partition_tokens=wl.partition_tokens, workspace=ws,
                     stream=stream, prepare=True))
+            elif fp8:
+                seq.append(pk.paged_attn_prefill_chunk_fp8(
+                    outs[L.name], d["q"], d["k_pool"], d["v_pool"], d["tables"], dev["_cu_q"],
+                    dev["_seq_lens"], int(wl.chunk_lens.max()), wl.scale, L.k_scale, L.v_scale,
+                    sliding_window=L.window, stream=stream, prepare=True))
             else:
                 seq.append(pk.paged_attn_prefill_chunk(
                     outs[L.name], d["q"], d["k_pool"], d["v_pool"], d["tables"], dev["_cu_q"],
@@ -391,6 +421,7 @@ def main():
             "block_size": wl.block_size, "max_seq_len": wl.max_seq_len,
             "layers": [L.name for L in wl.layers], "waves_rotated": R,
             "pool_blocks": [L.num_blocks for L in wl.layers if not L.alias_of],
+            "kv_dtype": "fp8_e4m3" if fp8 else wl.dtype,
         },
         "roofline": {
             "kernel": kern,
@@ -399,7 +430,7 @@ def main():
             "peak": peak,
             "unit": runit,
             "frac": round(achieved / peak, 4),
-            "traffic": counter_traffic(kern, args.workload),
+            "traffic": counter_traffic(kern, args.workload + ("_fp8" if fp8 else "")),
             "avg_launch_us": round(k_ms * 1e3 / max(k_n, 1), 3),
             "launches": k_n,
             "work_per_step": work,
