@@ -35,7 +35,11 @@ HIP_FLAGS = [
 ]
 # Per-source additions. The prefill kernel takes finite inputs only: without
 # NaN semantics its row maxima need no operand canonicalisation.
-HIP_EXTRA = {"prefill.hip": ["-fno-honor-nans"]}
+# decode.hip: matrix-core results in ordinary vector registers (the stage
+# loop's accumulators would otherwise be copied between register files every
+# stage).
+HIP_EXTRA = {"prefill.hip": ["-fno-honor-nans"],
+             "decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-I", CSRC]
 
 

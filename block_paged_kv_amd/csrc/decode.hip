@@ -402,16 +402,25 @@ __device__ __forceinline__ floatx4_t mfma_k16(const uint2& a, const uint2& b, fl
 // does not attend, so those LDS rows hold finite zeros.
 __device__ __attribute__((aligned(16))) const uint4 kZeroChunk = {0u, 0u, 0u, 0u};
 
-// global_load_lds_dwordx4: each lane copies 16 bytes from its own global
-// address to lds_dst + 16 * lane. Issued as assembly so that the compiler
-// leaves the vector-memory counter to the stage pipeline below (it would
-// otherwise drain every outstanding load before each LDS read). M0 holds the
-// destination; nothing else in these kernels uses M0.
-__device__ __forceinline__ void lds_dma16(const void* gaddr, const void* lds_dst) {
-  const uint32_t dst = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)(lds_dst))));
+// global_load_lds_dwordx4: each lane copies 16 bytes from global memory to
+// LDS byte offset m0 + 16 * lane (m0 wave-uniform). Issued as assembly so that
+// the compiler leaves the vector-memory counter to the stage pipeline below
+// (it would otherwise drain every outstanding load before each LDS read).
+// Two address forms: a 64-bit address per lane, or a wave-uniform 64-bit base
+// (held in scalar registers) plus a 32-bit byte offset per lane.
+__device__ __forceinline__ void lds_dma16(const void* gaddr, uint32_t m0) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :: "s"(dst), "v"(gaddr) : "memory");
+               :: "s"(m0), "v"(gaddr) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(m0), "v"(voff), "s"(base) : "memory", "m0");
+}
+
+// LDS byte offset of a __shared__ location: the low half of its generic
+// address (the high half is the LDS aperture).
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
 }
 
 // Wait until at most N vector-memory operations of this wave are in flight.
@@ -448,7 +457,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_lds_kernel(D
   const int s0 = (lo >> a.bs_log2) << a.bs_log2;
   const int ps = s0 + p * a.part;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nw = blockDim.x >> 6;
   const int lq = lane & 15;
   const int lg = lane >> 4;
@@ -502,31 +511,38 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_lds_kernel(D
   int tbl = 0;
   auto phys_ok = [&](int phys) { return phys > 0 && phys < a.nb; };
 
-  // Lane offsets (elements) inside a block for each load instruction: the
+  // Lane byte offsets inside a block for each load instruction: the
   // instruction's token row i*TPI + lane/CPT, global chunk (lane%CPT) ^ row.
-  uint32_t lane_off[NI];
+  uint32_t voff[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int row = i * TPI + lane / CPT;
     const int chunk = (lane % CPT) ^ (row & SWZ);
-    lane_off[i] = static_cast<uint32_t>((row & (bs8 ? 7 : 15)) * D + chunk * EPC);
+    voff[i] = static_cast<uint32_t>(((row & (bs8 ? 7 : 15)) * D + chunk * EPC) * ESZ);
   }
+  // With block size 8 one instruction spans both blocks of a stage only when
+  // it covers more than 8 rows (64-byte rows); such stages take the per-lane
+  // address form.
+  const bool split_rows = bs8 && TPI > 8;
   const char* kpool = static_cast<const char*>(a.k_pool);
   const char* vpool = static_cast<const char*>(a.v_pool);
 
-  // Issue the loads of stage k (0-based within this wave) into ring slot sb:
-  // exactly 2*NI load instructions, every lane active (rows the stage does
-  // not attend read the zero chunk). Returns the stage's valid-token mask
-  // (bit t: token ts + t is attended and its block id is valid). The block
-  // ids come from the table window, loaded before any stage is in flight.
-  auto issue = [&](int k, uint4* sb) -> uint32_t {
+  // Issue the loads of stage k (0-based within this wave) into the ring slot
+  // at LDS offset sl: exactly 2*NI load instructions, every lane active.
+  // Returns the stage's valid-token mask (bit t: token ts + t is attended and
+  // its block id is valid). The block ids come from the table window, loaded
+  // before any stage is in flight. A stage whose 16 rows are all valid loads
+  // from the block base (scalar) plus the lane's fixed offset; any other stage
+  // gives each lane its own address, rows it does not attend reading the zero
+  // chunk.
+  auto issue = [&](int k, uint32_t sl) -> uint32_t {
     const int ts = ts0 + k * kStageTokens;
     const int blk = ts >> bs_log2;
     const int phys_lo = __builtin_amdgcn_readlane(tbl, blk - tb0);
     const int phys_hi = __builtin_amdgcn_readlane(tbl, bs8 ? blk + 1 - tb0 : blk - tb0);
     const size_t sub = static_cast<size_t>(ts & bs_mask) * D;
-    const size_t base_lo = ((static_cast<size_t>(phys_lo) * a.hkv + kvh) << bs_log2) * D + sub;
-    const size_t base_hi = ((static_cast<size_t>(phys_hi) * a.hkv + kvh) << bs_log2) * D + sub;
+    const size_t base_lo = (((static_cast<size_t>(phys_lo) * a.hkv + kvh) << bs_log2) * D + sub) * ESZ;
+    const size_t base_hi = (((static_cast<size_t>(phys_hi) * a.hkv + kvh) << bs_log2) * D + sub) * ESZ;
     const int v0 = min(max(t_begin - ts, 0), kStageTokens);
     const int v1 = min(max(t_end - ts, 0), kStageTokens);
     uint32_t vmask = v1 > v0 ? ((0xFFFFu >> (kStageTokens - v1)) & ~((1u << v0) - 1u)) : 0u;
@@ -535,18 +551,26 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_lds_kernel(D
     // The slot's previous stage has been consumed; its LDS reads must have
     // returned before the new data lands.
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (vmask == 0xFFFFu && !split_rows) {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      // Row i*TPI + lane/CPT of the stage; with block size 8, rows 8..15 are in
-      // the second block (one instruction covers both at 64-byte rows).
-      const int row = i * TPI + lane / CPT;
-      const size_t base = (bs8 && row >= 8) ? base_hi : base_lo;
-      const bool ok = (vmask >> row) & 1u;
-      const size_t off = (base + lane_off[i]) * ESZ;
-      const void* ksrc = ok ? static_cast<const void*>(kpool + off) : &kZeroChunk;
-      const void* vsrc = ok ? static_cast<const void*>(vpool + off) : &kZeroChunk;
-      lds_dma16(ksrc, sb + i * 64);
-      lds_dma16(vsrc, sb + SBYTES / 16 + i * 64);
+      for (int i = 0; i < NI; ++i) {
+        // With block size 8, rows 8..15 are in the second block.
+        const size_t base = (bs8 && i * TPI >= 8) ? base_hi : base_lo;
+        lds_dma16(kpool + base, voff[i], sl + i * 1024);
+        lds_dma16(vpool + base, voff[i], sl + SBYTES + i * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int row = i * TPI + lane / CPT;
+        const size_t base = (bs8 && row >= 8) ? base_hi : base_lo;
+        const bool ok = (vmask >> row) & 1u;
+        const size_t off = base + voff[i];
+        const void* ksrc = ok ? static_cast<const void*>(kpool + off) : &kZeroChunk;
+        const void* vsrc = ok ? static_cast<const void*>(vpool + off) : &kZeroChunk;
+        lds_dma16(ksrc, sl + i * 1024);
+        lds_dma16(vsrc, sl + SBYTES + i * 1024);
+      }
     }
     return vmask;
   };
@@ -650,6 +674,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_lds_kernel(D
   constexpr int OPS = 2 * NI;  // load instructions per stage
   uint4* const slot0 = &ring0[wave][0];
   uint4* const slot1 = &ring1[wave][0];
+  const uint32_t lds0 = lds_offset(slot0);
+  const uint32_t lds1 = lds_offset(slot1);
   // Stages per window: an even count whose blocks (plus a block-size
   // misalignment of the first stage) stay within 64 table entries.
   const int spwin = ((63 << bs_log2) / kStageTokens) & ~1;
@@ -663,16 +689,16 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_lds_kernel(D
       tbl = (lb < blk_end && lb < a.mb) ? bt[lb] : 0;
     }
     vm_wait<0>();  // the window's block ids (and, first time, the query) have arrived
-    uint32_t mask0 = issue(w0, slot0);
-    uint32_t mask1 = w0 + 1 < w1 ? issue(w0 + 1, slot1) : 0u;
+    uint32_t mask0 = issue(w0, lds0);
+    uint32_t mask1 = w0 + 1 < w1 ? issue(w0 + 1, lds1) : 0u;
     for (int k = w0; k < w1; k += 2) {
       if (k + 1 < w1) vm_wait<OPS>(); else vm_wait<0>();
       compute(slot0, mask0);
-      if (k + 2 < w1) mask0 = issue(k + 2, slot0);
+      if (k + 2 < w1) mask0 = issue(k + 2, lds0);
       if (k + 1 < w1) {
         if (k + 2 < w1) vm_wait<OPS>(); else vm_wait<0>();
         compute(slot1, mask1);
-        if (k + 3 < w1) mask1 = issue(k + 3, slot1);
+        if (k + 3 < w1) mask1 = issue(k + 3, lds1);
       }
     }
   }
