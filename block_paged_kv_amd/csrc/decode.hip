@@ -587,21 +587,6 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_lds_kernel(D
   auto compute = [&](const uint4* sb, uint32_t vmask) {
     const char* kr = reinterpret_cast<const char*>(sb);
     const char* vr_in = kr + SBYTES;
-    // ---- S^T = K Q^T --------------------------------------------------------
-    // A operand: key lq, head_dim elements 32*ks + 8*lg .. +8.
-    floatx4_t s = floatx4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      uint4 ka;
-      if constexpr (KV8) {
-        const int chunk = (2 * ks + (lg >> 1)) ^ (lq & SWZ);
-        ka = widen_e4m3x8(*reinterpret_cast<const uint2*>(kr + lq * ROWB + chunk * 16 + 8 * (lg & 1)));
-      } else {
-        const int chunk = (4 * ks + lg) ^ (lq & SWZ);
-        ka = *reinterpret_cast<const uint4*>(kr + lq * ROWB + chunk * 16);
-      }
-      s = mfma_k32(ka, qb[ks], s);
-    }
     // FP8: widen the stage's V rows into this wave's bf16 tile (same row
     // layout as the bf16 kernel reads). Only this wave touches the tile, and a
     // wave's LDS accesses are performed in order.
@@ -621,6 +606,34 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_lds_kernel(D
       }
       vr_bf = vw;
     }
+    // Every LDS read of the stage is requested up front: the A operand of
+    // S^T = K Q^T (key lq, head_dim elements 32*ks + 8*lg .. +8) and the B
+    // operand of O += P V. For the latter, lane (lq, lg) addresses key row
+    // 4*lg + lq/4, columns 16*nt + 4*(lq%4) .. +3; the transposing read
+    // returns keys 4*lg .. 4*lg+3 of column 16*nt + lq.
+    uint4 ka[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if constexpr (KV8) {
+        const int chunk = (2 * ks + (lg >> 1)) ^ (lq & SWZ);
+        ka[ks] = widen_e4m3x8(*reinterpret_cast<const uint2*>(kr + lq * ROWB + chunk * 16 + 8 * (lg & 1)));
+      } else {
+        const int chunk = (4 * ks + lg) ^ (lq & SWZ);
+        ka[ks] = *reinterpret_cast<const uint4*>(kr + lq * ROWB + chunk * 16);
+      }
+    }
+    const int vrow = 4 * lg + (lq >> 2);
+    const char* vr = vr_bf + vrow * VROWB + 8 * (lq & 1);
+    uint2 vb[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int chunk = (2 * nt + ((lq & 3) >> 1)) ^ (vrow & VSWZ);
+      vb[nt] = ds_read_tr16(reinterpret_cast<const uint16_t*>(vr + chunk * 16));
+    }
+    // ---- S^T = K Q^T --------------------------------------------------------
+    floatx4_t s = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) s = mfma_k32(ka[ks], qb[ks], s);
     // ---- mask (stages that straddle the range or hold an invalid block) ------
     if (vmask != 0xFFFFu) {
       // The empty asm keeps the per-key tests inside this rarely taken branch.
@@ -651,17 +664,9 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_lds_kernel(D
     pa.x = pack_bf16x2(fast_exp2(fmaf(s[0], c, negc)), fast_exp2(fmaf(s[1], c, negc)));
     pa.y = pack_bf16x2(fast_exp2(fmaf(s[2], c, negc)), fast_exp2(fmaf(s[3], c, negc)));
     // ---- O += P V ---------------------------------------------------------------
-    // Lane (lq, lg) addresses key row 4*lg + lq/4, columns 16*nt + 4*(lq%4) .. +3;
-    // the transposing read returns keys 4*lg .. 4*lg+3 of column 16*nt + lq.
-    const int vrow = 4 * lg + (lq >> 2);
-    const char* vr = vr_bf + vrow * VROWB + 8 * (lq & 1);
     lsum = mfma_k16(pa, ones, lsum);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int chunk = (2 * nt + ((lq & 3) >> 1)) ^ (vrow & VSWZ);
-      const uint2 vb = ds_read_tr16(reinterpret_cast<const uint16_t*>(vr + chunk * 16));
-      o[nt] = mfma_k16(pa, vb, o[nt]);
-    }
+    for (int nt = 0; nt < NT; ++nt) o[nt] = mfma_k16(pa, vb[nt], o[nt]);
   };
 
   // ---- stream: one stage landing while the other computes ------------------
@@ -704,32 +709,53 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_lds_kernel(D
   }
 
   // ---- merge the waves and store -------------------------------------------
-  // (max, sum, accumulator) of each wave to LDS, reusing the rings once every
-  // wave is done with them.
+  // Each wave puts its (max, sum) and accumulator rows in its own ring slots
+  // (only it has used them), so one barrier suffices before the merge.
+  {
+    float* my_o = reinterpret_cast<float*>(&ring0[wave][0]);   // [16][D]
+    float* my_ml = reinterpret_cast<float*>(&ring1[wave][0]);  // [16][2]
+    static_assert(Sg::SLOT0 >= 16 * D * static_cast<int>(sizeof(float)), "merge buffer does not fit");
+    // Lanes holding any of the GT real rows write all four of theirs (rows
+    // up to 15 stay inside the slot).
+    if (4 * lg < GT) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) my_o[(4 * lg + i) * D + 16 * nt + lq] = o[nt][i];
+      if (lq == 0)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) my_ml[(4 * lg + i) * 2 + 1] = lsum[i];
+    }
+    if (lg == 0 && lq < GT) my_ml[lq * 2] = mc;
+  }
   __syncthreads();
-  float* sm_o = reinterpret_cast<float*>(ring0);   // [nw][16][D]
-  float* sm_ml = reinterpret_cast<float*>(ring1);  // [nw][16][2]
-  static_assert(sizeof(ring0) >= kDecodeWaves * 16 * D * sizeof(float), "merge buffer does not fit");
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sm_o[(wave * 16 + 4 * lg + i) * D + 16 * nt + lq] = o[nt][i];
-  if (lg == 0) sm_ml[(wave * 16 + lq) * 2] = mc;
-  if (lq == 0)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sm_ml[(wave * 16 + 4 * lg + i) * 2 + 1] = lsum[i];
-  __syncthreads();
+  const float* sm_o = reinterpret_cast<const float*>(ring0);
+  const float* sm_ml = reinterpret_cast<const float*>(ring1);
+  constexpr int kO = Sg::SLOT0 / 4;      // floats between two waves' accumulator rows
+  constexpr int kML = 2 * SBYTES / 4;    // floats between two waves' (max, sum) rows
   for (int idx = threadIdx.x; idx < GT * D; idx += blockDim.x) {
     const int g = idx / D;
     const int d = idx - g * D;
+    // Every wave slot is read at once (all lie inside the rings); the entries
+    // of waves past nw, which did not run, are then ignored.
+    float mw[kDecodeWaves], lw[kDecodeWaves], ow[kDecodeWaves];
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) {
+      const float2 ml = *reinterpret_cast<const float2*>(sm_ml + w * kML + g * 2);
+      mw[w] = ml.x;
+      lw[w] = ml.y;
+      ow[w] = sm_o[w * kO + g * D + d];
+    }
     float M = kNegInf;
-    for (int w = 0; w < nw; ++w) M = fmaxf(M, sm_ml[(w * 16 + g) * 2]);
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) M = w < nw ? fmaxf(M, mw[w]) : M;
     float L = 0.f, A = 0.f;
-    for (int w = 0; w < nw; ++w) {
-      const float mw = sm_ml[(w * 16 + g) * 2];
-      const float f = mw == kNegInf ? 0.f : fast_exp2(mw - M);
-      L += sm_ml[(w * 16 + g) * 2 + 1] * f;
-      A += sm_o[(w * 16 + g) * D + d] * f;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) {
+      const bool live = w < nw && mw[w] != kNegInf;
+      const float f = live ? fast_exp2(mw[w] - M) : 0.f;
+      L = live ? fmaf(lw[w], f, L) : L;
+      A = live ? fmaf(ow[w], f, A) : A;
     }
     const size_t bh = static_cast<size_t>(b) * a.hq + h0 + g;
     A *= a.v_scale;  // FP8: V codes stand for v_scale * value (1 for bf16: exact)

@@ -88,14 +88,16 @@ __device__ __forceinline__ float max_across_groups(float x) {
 }
 
 // Eight E4M3 codes (bytes of v, low first) to eight bf16 values, exactly:
-// every E4M3 value is a bf16 value.
+// every E4M3 value is a bf16 value. v_cvt_scalef32_pk_bf16_fp8 converts one
+// 16-bit half of a word (two codes) and multiplies by 2^exponent(scale); a
+// scale of 1 leaves the values as they are.
+template <bool HI>
+__device__ __forceinline__ uint32_t widen_e4m3x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
 __device__ __forceinline__ uint4 widen_e4m3x8(const uint2& v) {
-  const auto f0 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(v.x), false);
-  const auto f1 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(v.x), true);
-  const auto f2 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(v.y), false);
-  const auto f3 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(v.y), true);
-  return make_uint4(pack_bf16x2(f0[0], f0[1]), pack_bf16x2(f1[0], f1[1]),
-                    pack_bf16x2(f2[0], f2[1]), pack_bf16x2(f3[0], f3[1]));
+  return make_uint4(widen_e4m3x2<false>(v.x), widen_e4m3x2<true>(v.x),
+                    widen_e4m3x2<false>(v.y), widen_e4m3x2<true>(v.y));
 }
 
 }  // namespace pagedkv
