@@ -175,9 +175,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodePa
   __shared__ float sm_m[kMaxWaves][GT];
   __shared__ float sm_l[kMaxWaves][GT];
 
-  const int p = blockIdx.x;
-  const int hg = blockIdx.y;
-  const int b = blockIdx.z;
+  const int hg = blockIdx.x;
+  const int b = blockIdx.y;
+  const int p = blockIdx.z;
   const int kvh = hg / a.head_groups;
   const int h0 = kvh * a.group + (hg - kvh * a.head_groups) * GT;
   const int n = a.seq_lens[b];
@@ -446,9 +446,9 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_lds_kernel(D
   // FP8: each wave's V stage widened to bf16 rows for the transposing read.
   __shared__ uint4 vwide[KV8 ? kDecodeWaves : 1][KV8 ? 16 * VROWB / 16 : 1];
 
-  const int p = blockIdx.x;
-  const int hg = blockIdx.y;
-  const int b = blockIdx.z;
+  const int hg = blockIdx.x;
+  const int b = blockIdx.y;
+  const int p = blockIdx.z;
   const int GT = a.gt;
   const int kvh = hg / a.head_groups;
   const int h0 = kvh * a.group + (hg - kvh * a.head_groups) * GT;
@@ -1083,6 +1083,10 @@ int32_t decode_impl(void* out, const void* q, const void* k_pool, const void* v_
     return fail(PAGED_ERR_INVALID_ARG, "k_scale and v_scale must be finite and positive");
   if (batch > 65535 || num_q_heads > 65535)
     return fail(PAGED_ERR_INVALID_ARG, "batch and num_q_heads must be at most 65535");
+  if (pl.max_parts > 65535)
+    return fail(PAGED_ERR_INVALID_ARG,
+                "max_seq_len %d needs %d partitions of %d tokens; at most 65535 are supported",
+                max_seq_len, pl.max_parts, pl.part);
   if (batch == 0) return ok();
   if (!out || !q || !k_pool || !v_pool || !block_tables || !seq_lens)
     return fail(PAGED_ERR_INVALID_ARG, "NULL pointer");
@@ -1120,9 +1124,13 @@ int32_t decode_impl(void* out, const void* q, const void* k_pool, const void* v_
   prm.scale_log2 = scale * 1.4426950408889634f * k_scale;
   prm.v_scale = v_scale;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 grid(static_cast<unsigned>(pl.max_parts),
-                  static_cast<unsigned>(num_kv_heads * prm.head_groups),
-                  static_cast<unsigned>(batch));
+  // Partition index slowest: a row whose span is shorter than max_seq_len
+  // leaves its later partitions empty, and those workgroups (which only read
+  // the row length before leaving) are then dispatched together near the end
+  // instead of holding slots between the streaming ones.
+  const dim3 grid(static_cast<unsigned>(num_kv_heads * prm.head_groups),
+                  static_cast<unsigned>(batch),
+                  static_cast<unsigned>(pl.max_parts));
   const dim3 block(static_cast<unsigned>(64 * pl.nw));
   {
     LaunchTrace tr(PAGED_KERNEL_DECODE_PARTIAL, s);
