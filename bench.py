@@ -18,7 +18,7 @@ the dominant kernel (its average launch time from HIP events recorded by the
 library on the launch stream over the timed region) and the CPU oracle's rate
 on a bounded sample of the same workload.
 
-    python bench.py [--workload qwen3|mixed|hybrid|prefill|tiny] [--kv bf16|fp8]
+    python bench.py [--workload qwen3|mixed|hybrid|prefill|hprefill|tiny] [--kv bf16|fp8]
                     [--steps K] [--warmup W]
 
 ``--kv fp8`` runs the same workload over FP8 (E4M3) pools with per-layer
@@ -43,7 +43,7 @@ KERNEL_SOURCES = {"decode_partial": ["decode.hip", "device.h"], "prefill": ["pre
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 DEFAULT_WAVES = {"qwen3": 16}
-DEFAULT_STEPS = {"qwen3": 1000, "mixed": 200, "hybrid": 200, "prefill": 30, "tiny": 500}
+DEFAULT_STEPS = {"qwen3": 1000, "mixed": 200, "hybrid": 200, "prefill": 30, "hprefill": 30, "tiny": 500}
 
 
 def log(msg):
@@ -90,19 +90,21 @@ def _only(wl, L):
 
 
 def prefill_flops(wl, rows=None):
-    """4 * D per (query head, visible key) pair: Q.K and P.V, multiply-adds x2."""
+    """4 * D per (query head, visible key) pair: Q.K and P.V, multiply-adds x2,
+    summed over the workload's layers (each with its own window)."""
     pairs = 0
     cu = np.concatenate([[0], np.cumsum(wl.chunk_lens)])
-    for b in range(wl.batch):
-        C = int(wl.chunk_lens[b])
-        P = int(wl.seq_lens[b]) - C
-        W = wl.layers[0].window
-        for i in range(C):
-            if rows is not None and int(cu[b]) + i not in rows:
-                continue
-            a = P + i
-            lo = max(0, a - W + 1) if W else 0
-            pairs += a + 1 - lo
+    for L in wl.layers:
+        W = L.window
+        for b in range(wl.batch):
+            C = int(wl.chunk_lens[b])
+            P = int(wl.seq_lens[b]) - C
+            for i in range(C):
+                if rows is not None and int(cu[b]) + i not in rows:
+                    continue
+                a = P + i
+                lo = max(0, a - W + 1) if W else 0
+                pairs += a + 1 - lo
     return 4.0 * wl.head_dim * wl.hq * pairs
 
 
@@ -221,7 +223,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="qwen3", choices=["qwen3", "mixed", "hybrid", "prefill", "tiny"])
+    ap.add_argument("--workload", default="qwen3", choices=["qwen3", "mixed", "hybrid", "prefill", "hprefill", "tiny"])
     ap.add_argument("--waves", type=int, default=None, help="independent batches rotated through")
     ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"], help="KV pool element type")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -393,10 +395,10 @@ def main():
         ms, n = pk.trace_query(name)
         if n:
             kernels[name] = {"launches": n, "avg_us": round(ms * 1e3 / n, 3)}
-    if wl.kind == "decode" and len(wl.layers) > 1:
-        # partial launches cycle through the layers in order within a step
-        dur = pk.trace_durations("decode_partial")
-        kernels["decode_partial_by_layer_avg_us"] = {
+    if len(wl.layers) > 1:
+        # attention launches cycle through the layers in order within a step
+        dur = pk.trace_durations(kern)
+        kernels[f"{kern}_by_layer_avg_us"] = {
             L.name: round(float(np.mean(dur[i::len(wl.layers)])) * 1e3, 3) for i, L in enumerate(wl.layers)}
     log(f"[bench] kernels: {kernels}")
 
@@ -416,7 +418,9 @@ def main():
         "config": {
             "workload": {"qwen3": "qwen3-0.6b-shaped decode step", "mixed": "mixed-length continuous-batching decode",
                          "hybrid": "gemma-style hybrid sliding/full/kv-shared decode",
-                         "prefill": "chunked prefill over cached prefix", "tiny": "tiny fp32 decode"}[args.workload],
+                         "prefill": "chunked prefill over cached prefix",
+                         "hprefill": "gemma-style hybrid sliding/full/kv-shared chunked prefill",
+                         "tiny": "tiny fp32 decode"}[args.workload],
             "batch": int(wsz), "num_q_heads": wl.hq, "num_kv_heads": wl.hkv, "head_dim": wl.head_dim,
             "block_size": wl.block_size, "max_seq_len": wl.max_seq_len,
             "layers": [L.name for L in wl.layers], "waves_rotated": R,

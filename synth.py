@@ -24,6 +24,12 @@ rounded to bf16 with round-to-nearest-even for bf16 workloads):
 * ``prefill`` -- chunked prefill: B=1, Hq=32, Hkv=8, D=128, bf16, a 2048-token
                  chunk over a 63488-token cached prefix (65536-token context,
                  4096 blocks of a 32768-block pool), chunk K/V written first.
+* ``hprefill`` -- Gemma-style hybrid chunked prefill: B=4, Hq=8, Hkv=1, D=256,
+                 bf16, a 2048-token chunk per row over a 6144-token cached prefix;
+                 the same three layers as ``hybrid`` (sliding window 512 with its
+                 own 1024-block pool and null entries for expired blocks, full
+                 attention, and a KV-shared layer reading the full layer's pool
+                 and tables, which writes nothing).
 
 Random draw order per workload (``numpy.random.default_rng(seed)``): the
 allocator free-list permutation, then lengths and prefix choices, then the
@@ -38,7 +44,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 BLOCK_SIZE = 16
-SEEDS = {"tiny": 1000, "qwen3": 1001, "mixed": 1002, "hybrid": 1003, "prefill": 1004}
+SEEDS = {"tiny": 1000, "qwen3": 1001, "mixed": 1002, "hybrid": 1003, "prefill": 1004, "hprefill": 1005}
 
 
 def round_bf16(x):
@@ -225,6 +231,38 @@ def _make(name, rng, bs, *, batch=None, hq=None, hkv=None, head_dim=None, contex
             layer.k[b] = np.concatenate([layer.k[b], _normal(rng, (int(C[b]), Hkv, D), True)])
             layer.v[b] = np.concatenate([layer.v[b], _normal(rng, (int(C[b]), Hkv, D), True)])
         return Workload(name, "prefill", B, Hq, Hkv, D, "bf16", lens, toks, [layer],
+                        1.0 / math.sqrt(D), chunk_lens=C, block_size=bs)
+
+    if name == "hprefill":
+        B, Hq, Hkv, D = batch or 4, hq or 8, hkv or 1, head_dim or 256
+        NB = num_blocks or 32768
+        NBS = sliding_blocks or 1024
+        W = 512 if window is None else window
+        free_full = rng.permutation(np.arange(1, NB)).astype(np.int32)
+        free_slide = rng.permutation(np.arange(1, NBS)).astype(np.int32)
+        C = np.array(chunk if chunk is not None else [2048] * B, dtype=np.int32).reshape(-1)
+        P = np.array(context if context is not None else [6144] * B, dtype=np.int32).reshape(-1)
+        lens = (P + C).astype(np.int32)
+        layers = [Layer("sliding", NBS, W, None, free_slide), Layer("full", NB, 0, None, free_full),
+                  Layer("shared", NB, 0, "full", None)]
+        toks = [_suffix_tokens(b, int(lens[b])) for b in range(B)]
+        for L in layers:  # cached prefix K/V per layer (a sliding layer: from its first live block)
+            if L.alias_of:
+                continue
+            for b in range(B):
+                start = (max(0, int(P[b]) - W) // bs) * bs if W and L.window else 0
+                L.k.append(_normal(rng, (int(P[b]) - start, Hkv, D), True))
+                L.v.append(_normal(rng, (int(P[b]) - start, Hkv, D), True))
+                L.live_from.append(start)
+        for L in layers:
+            L.q = _normal(rng, (int(C.sum()), Hq, D), True)
+        for L in layers:  # the chunk's own K/V: the tokens the step writes
+            if L.alias_of:
+                continue
+            for b in range(B):
+                L.k[b] = np.concatenate([L.k[b], _normal(rng, (int(C[b]), Hkv, D), True)])
+                L.v[b] = np.concatenate([L.v[b], _normal(rng, (int(C[b]), Hkv, D), True)])
+        return Workload(name, "prefill", B, Hq, Hkv, D, "bf16", lens, toks, layers,
                         1.0 / math.sqrt(D), chunk_lens=C, block_size=bs)
 
     raise ValueError(f"unknown workload {name}")

@@ -83,6 +83,8 @@ def run_case(pk, wl, rows=None, label="", **step_kw):
     ("mixed", dict(batch=5, context=(20, 300), prefix=100, num_blocks=300, block_size=8)),
     ("hybrid", dict(batch=2, context=500, window=100, hq=8, hkv=1, head_dim=256, sliding_blocks=30,
                     num_blocks=100, block_size=64)),
+    ("hprefill", dict(batch=2, context=[300, 700], chunk=[100, 37], window=64, num_blocks=200,
+                      sliding_blocks=64)),
 ])
 def test_write_is_bit_exact(pk, name, kw):
     import torch
@@ -305,6 +307,33 @@ def test_prefill_full_size_sampled_rows(pk):
     rows = sorted(set([0, 1, 2, 31, 32, 127, 128, 1000, 1023, 1024, 2046, 2047] +
                       list(np.random.default_rng(5).integers(0, 2048, size=40))))
     run_case(pk, wl, rows=rows, label="prefill-full")
+
+
+HPREFILL_SMALL = [
+    dict(batch=2, context=[300, 700], chunk=[100, 37], window=64, num_blocks=200, sliding_blocks=64),
+    dict(batch=3, context=[0, 90, 513], chunk=[130, 1, 64], window=100, num_blocks=200, sliding_blocks=64),
+    dict(batch=2, context=[400, 33], chunk=[77, 200], window=48, num_blocks=300, sliding_blocks=80,
+         block_size=8),
+    dict(batch=2, context=[400, 33], chunk=[77, 200], window=200, num_blocks=100, sliding_blocks=40,
+         block_size=32),
+    dict(batch=1, context=[1000], chunk=[300], window=1, num_blocks=100, sliding_blocks=40, hq=4),
+]
+
+
+@pytest.mark.parametrize("kw", HPREFILL_SMALL, ids=[str(i) for i in range(len(HPREFILL_SMALL))])
+def test_hybrid_prefill_small(pk, kw):
+    """Gemma-style chunked prefill: sliding layer (own pool, null entries for
+    expired blocks), full layer, and a KV-shared layer over the full layer's
+    pool and tables; D=256, 8 query heads per KV head."""
+    run_case(pk, synth.make("hprefill", **kw), label="hprefill-small")
+
+
+def test_hybrid_prefill_full_size_sampled_rows(pk):
+    wl = synth.make("hprefill")
+    T = int(wl.chunk_lens.sum())
+    rows = sorted(set([0, 1, 2, 511, 512, 2047, 2048, 2049, 4095, 4096, 6143, 6144, T - 2, T - 1] +
+                      list(np.random.default_rng(6).integers(0, T, size=36))))
+    run_case(pk, wl, rows=rows, label="hprefill-full")
 
 
 def test_prefill_chunk_of_one_matches_decode(pk):
