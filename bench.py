@@ -226,6 +226,7 @@ def main():
     ap.add_argument("--workload", default="qwen3", choices=["qwen3", "mixed", "hybrid", "prefill", "hprefill", "tiny"])
     ap.add_argument("--waves", type=int, default=None, help="independent batches rotated through")
     ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"], help="KV pool element type")
+    ap.add_argument("--head-dim", type=int, default=None, help="head_dim override (e.g. 512 for the hybrid decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
@@ -256,6 +257,8 @@ def main():
             sys.exit(2)
         kw["kv_dtype"] = "fp8"
     fp8 = args.kv == "fp8"
+    if args.head_dim:
+        kw["head_dim"] = args.head_dim
     log(f"[bench] building workload {args.workload} ({kw})")
     wl = synth.make(args.workload, **kw)
     R = waves if args.workload == "qwen3" else 1

@@ -377,9 +377,23 @@ struct StageGeo {
   // widened into such a tile first).
   static constexpr int VROWB = D * 2;
   static constexpr int VSWZ = (VROWB / 16) < 16 ? (VROWB / 16) - 1 : 15;
-  // Ring slot 0 doubles as the wave-merge buffer (16 heads x D floats).
+  // Ring slots per wave: two (one stage landing while the other computes),
+  // one at head_dim 512, where a stage of K and V takes 32 KiB and four
+  // waves' rings must stay within the compute unit's LDS.
+  static constexpr int NSLOT = D >= 512 ? 1 : 2;
+  static constexpr int STAGE = 2 * SBYTES;                 // K then V rows of one stage
+  static constexpr int WIDE = ESZ == 1 ? 16 * VROWB : 0;   // FP8: the widened V rows
+  // Ring slot 0 doubles as the wave-merge buffer (16 heads x D floats); with
+  // one slot it also holds the widened V rows after the stage.
   static constexpr int MERGE = 16 * D * 4;
-  static constexpr int SLOT0 = 2 * SBYTES > MERGE ? 2 * SBYTES : MERGE;
+  static constexpr int SLOT0_DATA = NSLOT == 1 ? STAGE + WIDE : STAGE;
+  static constexpr int SLOT0 = SLOT0_DATA > MERGE ? SLOT0_DATA : MERGE;
+  // Slot 1 (two slots) or, with one slot, just the merge's (max, sum) rows.
+  static constexpr int SLOT1 = NSLOT == 2 ? STAGE : 16 * 2 * 4;
+  // LDS reads requested together: every K fragment and V operand of a stage,
+  // or (head_dim 512) half of them at a time, to bound the registers.
+  static constexpr int KB = KS < 8 ? KS : 8;
+  static constexpr int VB = NT < 16 ? NT : 16;
 };
 
 constexpr int kStageTokens = 16;
@@ -435,16 +449,19 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_lds_kernel(D
   constexpr bool KV8 = ESZ == 1;
   constexpr int CPT = Sg::CPT, TPI = Sg::TPI, NI = Sg::NI, KS = Sg::KS, NT = Sg::NT;
   constexpr int ROWB = Sg::ROWB, SWZ = Sg::SWZ, EPC = Sg::EPC, SBYTES = Sg::SBYTES;
-  constexpr int VROWB = Sg::VROWB, VSWZ = Sg::VSWZ;
+  constexpr int VROWB = Sg::VROWB, VSWZ = Sg::VSWZ, KB = Sg::KB, VB = Sg::VB;
   constexpr float kNegInf = -INFINITY;
 
   // One ring slot per array (K rows then V rows), so the compiler can tell the
   // slots apart when it orders LDS reads against the loads still writing
   // other slots. Slot 0 is padded to hold the wave-merge buffer.
+  constexpr int NSLOT = Sg::NSLOT;
   __shared__ uint4 ring0[kDecodeWaves][Sg::SLOT0 / 16];
-  __shared__ uint4 ring1[kDecodeWaves][2 * SBYTES / 16];
-  // FP8: each wave's V stage widened to bf16 rows for the transposing read.
-  __shared__ uint4 vwide[KV8 ? kDecodeWaves : 1][KV8 ? 16 * VROWB / 16 : 1];
+  __shared__ uint4 ring1[kDecodeWaves][Sg::SLOT1 / 16];
+  // FP8: each wave's V stage widened to bf16 rows for the transposing read
+  // (with one slot, inside slot 0 after the stage).
+  constexpr bool WIDE_ARRAY = KV8 && NSLOT == 2;
+  __shared__ uint4 vwide[WIDE_ARRAY ? kDecodeWaves : 1][WIDE_ARRAY ? Sg::WIDE / 16 : 1];
 
   const int hg = blockIdx.x;
   const int b = blockIdx.y;
@@ -592,7 +609,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_lds_kernel(D
     // wave's LDS accesses are performed in order.
     const char* vr_bf = vr_in;
     if constexpr (KV8) {
-      char* vw = reinterpret_cast<char*>(&vwide[wave][0]);
+      char* vw = WIDE_ARRAY ? reinterpret_cast<char*>(&vwide[wave][0])
+                            : reinterpret_cast<char*>(&ring0[wave][0]) + Sg::STAGE;
 #pragma unroll
       for (int j = 0; j < CPT / 4; ++j) {
         const int q = lane + 64 * j;  // fp8 chunk: row q / CPT, 16 elements (q % CPT)*16 ..
@@ -611,29 +629,43 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_lds_kernel(D
     // operand of O += P V. For the latter, lane (lq, lg) addresses key row
     // 4*lg + lq/4, columns 16*nt + 4*(lq%4) .. +3; the transposing read
     // returns keys 4*lg .. 4*lg+3 of column 16*nt + lq.
-    uint4 ka[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    auto read_k = [&](int ks) -> uint4 {
       if constexpr (KV8) {
         const int chunk = (2 * ks + (lg >> 1)) ^ (lq & SWZ);
-        ka[ks] = widen_e4m3x8(*reinterpret_cast<const uint2*>(kr + lq * ROWB + chunk * 16 + 8 * (lg & 1)));
+        return widen_e4m3x8(*reinterpret_cast<const uint2*>(kr + lq * ROWB + chunk * 16 + 8 * (lg & 1)));
       } else {
         const int chunk = (4 * ks + lg) ^ (lq & SWZ);
-        ka[ks] = *reinterpret_cast<const uint4*>(kr + lq * ROWB + chunk * 16);
+        return *reinterpret_cast<const uint4*>(kr + lq * ROWB + chunk * 16);
       }
-    }
+    };
     const int vrow = 4 * lg + (lq >> 2);
     const char* vr = vr_bf + vrow * VROWB + 8 * (lq & 1);
-    uint2 vb[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
+    auto read_v = [&](int nt) -> uint2 {
       const int chunk = (2 * nt + ((lq & 3) >> 1)) ^ (vrow & VSWZ);
-      vb[nt] = ds_read_tr16(reinterpret_cast<const uint16_t*>(vr + chunk * 16));
-    }
+      return ds_read_tr16(reinterpret_cast<const uint16_t*>(vr + chunk * 16));
+    };
     // ---- S^T = K Q^T --------------------------------------------------------
     floatx4_t s = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    uint2 vb[VB];
+    if constexpr (KB == KS) {
+      // Every K fragment and V operand of the stage requested at once.
+      uint4 ka[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) s = mfma_k32(ka[ks], qb[ks], s);
+      for (int ks = 0; ks < KS; ++ks) ka[ks] = read_k(ks);
+#pragma unroll
+      for (int nt = 0; nt < VB; ++nt) vb[nt] = read_v(nt);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) s = mfma_k32(ka[ks], qb[ks], s);
+    } else {
+#pragma unroll
+      for (int k0 = 0; k0 < KS; k0 += KB) {
+        uint4 ka[KB];
+#pragma unroll
+        for (int i = 0; i < KB; ++i) ka[i] = read_k(k0 + i);
+#pragma unroll
+        for (int i = 0; i < KB; ++i) s = mfma_k32(ka[i], qb[k0 + i], s);
+      }
+    }
     // ---- mask (stages that straddle the range or hold an invalid block) ------
     if (vmask != 0xFFFFu) {
       // The empty asm keeps the per-key tests inside this rarely taken branch.
@@ -665,8 +697,18 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_lds_kernel(D
     pa.y = pack_bf16x2(fast_exp2(fmaf(s[2], c, negc)), fast_exp2(fmaf(s[3], c, negc)));
     // ---- O += P V ---------------------------------------------------------------
     lsum = mfma_k16(pa, ones, lsum);
+    if constexpr (VB == NT) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) o[nt] = mfma_k16(pa, vb[nt], o[nt]);
+      for (int nt = 0; nt < NT; ++nt) o[nt] = mfma_k16(pa, vb[nt], o[nt]);
+    } else {
+#pragma unroll
+      for (int n0 = 0; n0 < NT; n0 += VB) {
+#pragma unroll
+        for (int i = 0; i < VB; ++i) vb[i] = read_v(n0 + i);
+#pragma unroll
+        for (int i = 0; i < VB; ++i) o[n0 + i] = mfma_k16(pa, vb[i], o[n0 + i]);
+      }
+    }
   };
 
   // ---- stream: one stage landing while the other computes ------------------
@@ -694,16 +736,27 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_lds_kernel(D
       tbl = (lb < blk_end && lb < a.mb) ? bt[lb] : 0;
     }
     vm_wait<0>();  // the window's block ids (and, first time, the query) have arrived
-    uint32_t mask0 = issue(w0, lds0);
-    uint32_t mask1 = w0 + 1 < w1 ? issue(w0 + 1, lds1) : 0u;
-    for (int k = w0; k < w1; k += 2) {
-      if (k + 1 < w1) vm_wait<OPS>(); else vm_wait<0>();
-      compute(slot0, mask0);
-      if (k + 2 < w1) mask0 = issue(k + 2, lds0);
-      if (k + 1 < w1) {
-        if (k + 2 < w1) vm_wait<OPS>(); else vm_wait<0>();
-        compute(slot1, mask1);
-        if (k + 3 < w1) mask1 = issue(k + 3, lds1);
+    if constexpr (NSLOT == 2) {
+      uint32_t mask0 = issue(w0, lds0);
+      uint32_t mask1 = w0 + 1 < w1 ? issue(w0 + 1, lds1) : 0u;
+      for (int k = w0; k < w1; k += 2) {
+        if (k + 1 < w1) vm_wait<OPS>(); else vm_wait<0>();
+        compute(slot0, mask0);
+        if (k + 2 < w1) mask0 = issue(k + 2, lds0);
+        if (k + 1 < w1) {
+          if (k + 2 < w1) vm_wait<OPS>(); else vm_wait<0>();
+          compute(slot1, mask1);
+          if (k + 3 < w1) mask1 = issue(k + 3, lds1);
+        }
+      }
+    } else {
+      // One slot: stage k+1 is requested once stage k has been consumed (its
+      // LDS reads returned: issue() waits for them first).
+      uint32_t mask0 = issue(w0, lds0);
+      for (int k = w0; k < w1; ++k) {
+        vm_wait<0>();
+        compute(slot0, mask0);
+        if (k + 1 < w1) mask0 = issue(k + 1, lds0);
       }
     }
   }
@@ -732,7 +785,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_lds_kernel(D
   const float* sm_o = reinterpret_cast<const float*>(ring0);
   const float* sm_ml = reinterpret_cast<const float*>(ring1);
   constexpr int kO = Sg::SLOT0 / 4;      // floats between two waves' accumulator rows
-  constexpr int kML = 2 * SBYTES / 4;    // floats between two waves' (max, sum) rows
+  constexpr int kML = Sg::SLOT1 / 4;     // floats between two waves' (max, sum) rows
   for (int idx = threadIdx.x; idx < GT * D; idx += blockDim.x) {
     const int g = idx / D;
     const int d = idx - g * D;
@@ -913,8 +966,10 @@ int32_t make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, int3
                   int32_t max_seq_len, int32_t window, int32_t partition_tokens, int esz, Plan* pl) {
   if (batch < 0 || hq < 1 || hkv < 1 || hq % hkv != 0)
     return fail(PAGED_ERR_INVALID_ARG, "need num_q_heads a positive multiple of num_kv_heads");
-  if (head_dim != 64 && head_dim != 128 && head_dim != 256)
-    return fail(PAGED_ERR_INVALID_ARG, "head_dim must be 64, 128 or 256 (got %d)", head_dim);
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256 && head_dim != 512)
+    return fail(PAGED_ERR_INVALID_ARG, "head_dim must be 64, 128, 256 or 512 (got %d)", head_dim);
+  if (head_dim == 512 && esz > 2)
+    return fail(PAGED_ERR_INVALID_ARG, "head_dim 512 needs bf16 or FP8 pools (got float32)");
   if (!pow2_in(block_size, 8, 64))
     return fail(PAGED_ERR_INVALID_ARG, "block_size must be a power of two in [8, 64]");
   if (max_seq_len < 0 || window < 0) return fail(PAGED_ERR_INVALID_ARG, "negative length");
@@ -930,11 +985,11 @@ int32_t make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, int3
     const int32_t unit = std::max(kStageTokens, block_size);
     if (part == 0) {
       // Aim at every wave slot of the device busy at once (8 waves per CU, 4
-      // at head_dim 256 where a workgroup's rings take most of the LDS) with
+      // at head_dim 256 and 512 where a workgroup's rings take most of the LDS) with
       // whole stages per wave; longer rows get longer partitions.
       const int cus = device_cu_count();
       if (cus <= 0) return fail(PAGED_ERR_HIP, "cannot query the device compute-unit count");
-      const int64_t slots = static_cast<int64_t>(head_dim == 256 ? 4 : 8) * cus;
+      const int64_t slots = static_cast<int64_t>(head_dim >= 256 ? 4 : 8) * cus;
       const int64_t stages = pairs * ((span + kStageTokens - 1) / kStageTokens);
       int64_t spw = std::max<int64_t>(1, (stages + slots - 1) / slots);
       int64_t p2 = 1;
@@ -1004,7 +1059,8 @@ void launch_partial_any(const DecodeParams& prm, int kv_esz, int d, int gt, dim3
   if (kv_esz <= 2) {
     if (d == 64) launch_partial_stage<64>(prm, kv_esz, grid, block, s, tr);
     else if (d == 128) launch_partial_stage<128>(prm, kv_esz, grid, block, s, tr);
-    else launch_partial_stage<256>(prm, kv_esz, grid, block, s, tr);
+    else if (d == 256) launch_partial_stage<256>(prm, kv_esz, grid, block, s, tr);
+    else launch_partial_stage<512>(prm, kv_esz, grid, block, s, tr);
   } else {
     if (d == 64) launch_partial_f32<64>(prm, gt, grid, block, s, tr);
     else if (d == 128) launch_partial_f32<128>(prm, gt, grid, block, s, tr);
@@ -1018,8 +1074,10 @@ void launch_reduce_d(const DecodeParams& prm, int d, dim3 grid, hipStream_t s, c
     hipExtLaunchKernelGGL(decode_reduce_kernel<ESZ, 64>, grid, dim3(256), 0, s, tr.start(), tr.stop(), 0, prm);
   else if (d == 128)
     hipExtLaunchKernelGGL(decode_reduce_kernel<ESZ, 128>, grid, dim3(256), 0, s, tr.start(), tr.stop(), 0, prm);
-  else
+  else if (d == 256)
     hipExtLaunchKernelGGL(decode_reduce_kernel<ESZ, 256>, grid, dim3(256), 0, s, tr.start(), tr.stop(), 0, prm);
+  else if constexpr (ESZ == 2)
+    hipExtLaunchKernelGGL(decode_reduce_kernel<ESZ, 512>, grid, dim3(256), 0, s, tr.start(), tr.stop(), 0, prm);
 }
 
 }  // namespace

@@ -143,8 +143,8 @@ __global__ __launch_bounds__(kThreads) void kv_write_fp8_kernel(
 
 int32_t check_common(int32_t head_dim, int32_t block_size, int32_t num_kv_heads, int32_t dtype) {
   if (esize_of(dtype) == 0) return fail(PAGED_ERR_DTYPE, "unknown dtype %d", dtype);
-  if (head_dim != 64 && head_dim != 128 && head_dim != 256)
-    return fail(PAGED_ERR_INVALID_ARG, "head_dim must be 64, 128 or 256 (got %d)", head_dim);
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256 && head_dim != 512)
+    return fail(PAGED_ERR_INVALID_ARG, "head_dim must be 64, 128, 256 or 512 (got %d)", head_dim);
   if (!pow2_in(block_size, 8, 64))
     return fail(PAGED_ERR_INVALID_ARG, "block_size must be a power of two in [8, 64] (got %d)",
                 block_size);

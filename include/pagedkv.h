@@ -40,7 +40,8 @@
  *     Block 0 is the null sentinel and is never read.
  *   - A slot is physical_block * block_size + offset (int64); slot < 0 means
  *     padding.
- *   - head_dim in {64, 128, 256}; block_size a power of two in [8, 64];
+ *   - head_dim in {64, 128, 256} (also 512 for the KV write, the gather and
+ *     decode over bf16 or FP8 pools); block_size a power of two in [8, 64];
  *     num_q_heads a multiple of num_kv_heads (query head h reads KV head
  *     h / (num_q_heads / num_kv_heads)).
  *   - The allocator is host-only C++, not thread-safe (one allocator per pool,
@@ -141,7 +142,7 @@ int32_t paged_kv_gather(void* out_k, void* out_v, const void* k_pool, const void
 /* Partition size (tokens per split-K partition) that paged_attn_decode uses
  * when called with partition_tokens == 0, for these arguments and dtype.
  * bf16: the smallest power-of-two multiple of the workgroup's stage span
- * (16 tokens per wave, 8 waves, 4 at head_dim 256) that keeps every wave
+ * (16 tokens per wave, 8 waves, 4 at head_dim 256 and 512) that keeps every wave
  * slot of the device busy with whole stages (never below the block size).
  * fp32: the largest power of two in [64, 1024] that still gives at least 4
  * workgroups per compute unit, else 64. A pure function of its arguments and

@@ -89,7 +89,8 @@ def test_prefill_argument_errors():
 @pytest.mark.parametrize("B,hq,hkv,d,msl,w,part,dt", [
     (4, 16, 8, 128, 2048, 0, 128, "bf16"), (32, 32, 8, 128, 8192, 0, 512, "bf16"),
     (8, 8, 1, 256, 32768, 512, 64, "bf16"), (2, 4, 2, 64, 75, 0, 16, "f32"),
-    (3, 6, 3, 64, 100, 0, 128, "bf16"), (2, 4, 2, 64, 75, 0, 48, "f32")])
+    (3, 6, 3, 64, 100, 0, 128, "bf16"), (2, 4, 2, 64, 75, 0, 48, "f32"),
+    (8, 8, 1, 512, 32768, 0, 512, "bf16"), (8, 8, 1, 512, 32768, 512, 64, "fp8")])
 def test_workspace_bytes(B, hq, hkv, d, msl, w, part, dt):
     span = min(msl, w + 15) if w else msl
     parts = -(-span // part)
@@ -105,6 +106,19 @@ def test_partition_must_fit_the_kernel():
     with pytest.raises(pk.PagedError) as e:
         pk.paged_attn_decode_workspace_bytes(2, 4, 2, 64, 16, 100, 0, 64, "f16")
     assert e.value.code == pk.PAGED_ERR_DTYPE
+
+
+def test_head_dim_512_limits():
+    # decode takes head_dim 512 over bf16 and FP8 pools, not float32; prefill does not take it
+    assert pk.paged_attn_decode_workspace_bytes(2, 4, 2, 512, 16, 100, 0, 32, "bf16") > 0
+    with pytest.raises(pk.PagedError) as e:
+        pk.paged_attn_decode_workspace_bytes(2, 4, 2, 512, 16, 100, 0, 32, "f32")
+    assert e.value.code == pk.PAGED_ERR_INVALID_ARG
+    rc = pk.lib.paged_attn_prefill_chunk(None, None, None, None, None, 4, None, None, 1, 8, 8, 8, 8, 512,
+                                         16, 8, 0.1, 0, pk.PAGED_BF16, None)
+    assert rc == pk.PAGED_ERR_INVALID_ARG
+    assert pk.lib.paged_kv_write(None, None, None, None, None, 1, 8, 16, 1, 1024, 1, None) == \
+        pk.PAGED_ERR_INVALID_ARG
 
 
 def test_library_rule_needs_a_device_here():

@@ -133,6 +133,9 @@ FP8_DECODE = [
     ("hybrid", dict(batch=3, context=700, window=64, sliding_blocks=40, num_blocks=200), {}),
     ("hybrid", dict(batch=2, context=500, window=37, hq=4, hkv=2, head_dim=128, sliding_blocks=30,
                     num_blocks=100, block_size=32), dict(partition_tokens=32)),
+    ("hybrid", dict(batch=3, context=700, window=64, head_dim=512, sliding_blocks=40, num_blocks=200), {}),
+    ("mixed", dict(batch=5, hq=6, hkv=2, head_dim=512, context=(1, 300), prefix=32, num_blocks=200,
+                   block_size=8), dict(partition_tokens=32)),
 ]
 
 

@@ -85,6 +85,7 @@ def run_case(pk, wl, rows=None, label="", **step_kw):
                     num_blocks=100, block_size=64)),
     ("hprefill", dict(batch=2, context=[300, 700], chunk=[100, 37], window=64, num_blocks=200,
                       sliding_blocks=64)),
+    ("hybrid", dict(batch=2, context=300, window=64, head_dim=512, sliding_blocks=40, num_blocks=100)),
 ])
 def test_write_is_bit_exact(pk, name, kw):
     import torch
@@ -212,6 +213,29 @@ def test_decode_small(pk, name, kw, step):
 @pytest.mark.parametrize("name", ["tiny", "qwen3", "mixed", "hybrid"])
 def test_decode_full_size(pk, name):
     run_case(pk, synth.make(name), label="decode-full")
+
+
+# head_dim 512 (one ring slot per wave, LDS reads in halves): windows, block
+# sizes, explicit partitions, group sizes, 1-token rows.
+DECODE_D512 = [
+    ("hybrid", dict(batch=3, context=700, window=64, head_dim=512, sliding_blocks=40, num_blocks=200), {}),
+    ("hybrid", dict(batch=2, context=500, window=100, hq=4, hkv=2, head_dim=512, sliding_blocks=60,
+                    num_blocks=200, block_size=8), {}),
+    ("hybrid", dict(batch=2, context=500, window=37, hq=16, hkv=1, head_dim=512, sliding_blocks=30,
+                    num_blocks=100, block_size=64), dict(partition_tokens=64)),
+    ("mixed", dict(batch=5, hq=6, hkv=2, head_dim=512, context=(1, 300), prefix=32, num_blocks=200), {}),
+    ("mixed", dict(batch=5, hq=3, hkv=1, head_dim=512, context=(1, 400), prefix=64, num_blocks=200,
+                   block_size=32), dict(partition_tokens=32)),
+]
+
+
+@pytest.mark.parametrize("name,kw,step", DECODE_D512, ids=[f"{n}-{i}" for i, (n, _, _) in enumerate(DECODE_D512)])
+def test_decode_head_dim_512(pk, name, kw, step):
+    run_case(pk, synth.make(name, **kw), label="decode-d512", **step)
+
+
+def test_decode_head_dim_512_full_size(pk):
+    run_case(pk, synth.make("hybrid", head_dim=512), label="decode-d512-full")
 
 
 def test_decode_edge_lengths(pk):
