@@ -18,7 +18,7 @@ the dominant kernel (its average launch time from HIP events recorded by the
 library on the launch stream over the timed region) and the CPU oracle's rate
 on a bounded sample of the same workload.
 
-    python bench.py [--workload qwen3|mixed|hybrid|prefill|hprefill|tiny] [--kv bf16|fp8]
+    python bench.py [--workload qwen3|mixed|hybrid|prefill|hprefill|mixedstep|tiny] [--kv bf16|fp8]
                     [--steps K] [--warmup W]
 
 ``--kv fp8`` runs the same workload over FP8 (E4M3) pools with per-layer
@@ -43,7 +43,8 @@ KERNEL_SOURCES = {"decode_partial": ["decode.hip", "device.h"], "prefill": ["pre
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 DEFAULT_WAVES = {"qwen3": 16}
-DEFAULT_STEPS = {"qwen3": 1000, "mixed": 200, "hybrid": 200, "prefill": 30, "hprefill": 30, "tiny": 500}
+DEFAULT_STEPS = {"qwen3": 1000, "mixed": 200, "hybrid": 200, "prefill": 30, "hprefill": 30, "mixedstep": 100,
+                 "tiny": 500}
 
 
 def log(msg):
@@ -167,6 +168,14 @@ def cpu_baseline(wl, args):
         unit, scale = "GB/s", 1e9
         sample = f"oracle decode of {len(rows)} rows (every layer), repeated"
         fn = lambda: runner.oracle_step(sub, sub_pools)  # noqa: E731
+    elif wl.num_decode:
+        # continuous-batching step: the oracle over the step's decode rows (the
+        # metric's unit is their KV GB/s)
+        rows = list(range(wl.num_decode))
+        work = decode_bytes(wl, tabs, rows)
+        unit, scale = "GB/s", 1e9
+        sample = f"oracle over the {len(rows)} decode rows of the step (varlen prefill form), repeated"
+        fn = lambda: runner.oracle_step(wl, pools, rows=rows)  # noqa: E731
     else:
         T = int(wl.chunk_lens.sum())
         rows = sorted(set(np.linspace(0, T - 1, 128).astype(int).tolist()))
@@ -203,6 +212,50 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 5}), flush=True)
 
 
+def time_serial_mixed_step(pk, wl, dev, outs, ws, stream, steps):
+    """ms per step of the same continuous-batching step with its two parts one
+    after the other on one stream (decode rows, then the chunk rows), captured
+    and replayed like the timed region: the reference for the concurrent call."""
+    import torch
+
+    import runner
+
+    nd = wl.num_decode
+    calls = []
+    for L in wl.layers:
+        if L.alias_of:
+            continue
+        d = dev[L.name]
+        calls.append(pk.paged_kv_write(d["k_pool"], d["v_pool"], d["step_k"], d["step_v"], d["step_slots"],
+                                       stream=stream, prepare=True))
+    for L in wl.layers:
+        d = dev[L.name]
+        o = outs[L.name]
+        calls.append(pk.paged_attn_decode(o[:nd], d["q"][:nd], d["k_pool"], d["v_pool"], d["tables"][:nd],
+                                          dev["_seq_lens"][:nd], wl.scale, runner.decode_max_seq_len(wl),
+                                          sliding_window=L.window, partition_tokens=wl.partition_tokens,
+                                          workspace=ws, stream=stream, prepare=True))
+        calls.append(pk.paged_attn_prefill_chunk(o, d["q"], d["k_pool"], d["v_pool"], d["tables"][nd:],
+                                                 dev["_cu_q"][nd:], dev["_seq_lens"][nd:],
+                                                 int(wl.chunk_lens.max()), wl.scale, sliding_window=L.window,
+                                                 stream=stream, prepare=True))
+    with torch.cuda.stream(stream):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for _ in range(steps):
+            for c in calls:
+                c()
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
 def _subset(wl, rows):
     import copy
 
@@ -223,7 +276,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="qwen3", choices=["qwen3", "mixed", "hybrid", "prefill", "hprefill", "tiny"])
+    ap.add_argument("--workload", default="qwen3", choices=["qwen3", "mixed", "hybrid", "prefill", "hprefill", "mixedstep", "tiny"])
     ap.add_argument("--waves", type=int, default=None, help="independent batches rotated through")
     ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"], help="KV pool element type")
     ap.add_argument("--head-dim", type=int, default=None, help="head_dim override (e.g. 512 for the hybrid decode)")
@@ -262,6 +315,7 @@ def main():
     log(f"[bench] building workload {args.workload} ({kw})")
     wl = synth.make(args.workload, **kw)
     R = waves if args.workload == "qwen3" else 1
+    mixed_step = wl.kind == "prefill" and wl.num_decode > 0
     wsz = wl.wave_size or wl.batch
     tabs = synth.build_tables(pk.Allocator, wl)
     log("[bench] writing cached context to device pools")
@@ -298,7 +352,13 @@ def main():
                                              prepare=True))
         for L in wl.layers:
             d = dev[L.name]
-            if wl.kind == "decode" and fp8:
+            if mixed_step:
+                seq.append(pk.paged_attn_mixed(
+                    outs[L.name], d["q"], d["k_pool"], d["v_pool"], d["tables"], dev["_cu_q"], dev["_seq_lens"],
+                    wl.num_decode, int(wl.chunk_lens.max()), wl.scale, runner.decode_max_seq_len(wl),
+                    sliding_window=L.window, partition_tokens=wl.partition_tokens, workspace=ws,
+                    k_scale=L.k_scale, v_scale=L.v_scale, stream=stream, prepare=True))
+            elif wl.kind == "decode" and fp8:
                 seq.append(pk.paged_attn_decode_fp8(
                     outs[L.name], d["q"][rows], d["k_pool"], d["v_pool"], d["tables"][rows],
                     dev["_seq_lens"][rows], wl.scale, L.k_scale, L.v_scale, int(wl.seq_lens[rows].max()),
@@ -376,7 +436,34 @@ def main():
     torch.cuda.synchronize()
     pk.trace_enable(False)
 
-    if wl.kind == "decode":
+    extra = {}
+    if mixed_step:
+        # Decode rows' KV bytes over the step time is the value; the chunk's
+        # prefill carries the dominant kernel's roofline, the decode partial a
+        # second one (both timed while they share the device).
+        dec_rows = list(range(wl.num_decode))
+        T = int(wl.chunk_lens.sum())
+        dwork = decode_bytes(wl, tabs, dec_rows)
+        pwork = prefill_flops(wl, set(range(wl.num_decode, T)))
+        value = dwork / (ms_per_step * 1e-3) / 1e9
+        unit = "GB/s"
+        kern = "prefill"
+        k_ms, k_n = pk.trace_query(kern)
+        work = pwork
+        achieved = pwork * steps / (k_ms * 1e-3) / 1e12
+        peak, bound, runit = MFMA_BF16_PEAK_TFLOPS, "mfma", "TFLOP/s"
+        d_ms, d_n = pk.trace_query("decode_partial")
+        d_ach = dwork * steps / (d_ms * 1e-3) / 1e9
+        serial_ms = time_serial_mixed_step(pk, wl, dev, outs, ws, stream, steps)
+        extra = {
+            "roofline_decode": {"kernel": "decode_partial", "bound": "hbm", "achieved": round(d_ach, 3),
+                                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(d_ach / HBM_PEAK_GBS, 4),
+                                "avg_launch_us": round(d_ms * 1e3 / max(d_n, 1), 3), "work_per_step": dwork},
+            "prefill_tflops_in_step": round(pwork / (ms_per_step * 1e-3) / 1e12, 3),
+            "serial_ms_per_step": round(serial_ms, 6),
+            "speedup_vs_serial": round(serial_ms / ms_per_step, 4),
+        }
+    elif wl.kind == "decode":
         per_wave = [decode_bytes(wl, tabs, list(range(r * wsz, (r + 1) * wsz))) for r in range(R)]
         work = float(np.mean([per_wave[(args.warmup + i) % R] for i in range(steps)]))
         value = work / (ms_per_step * 1e-3) / 1e9
@@ -423,6 +510,7 @@ def main():
                          "hybrid": "gemma-style hybrid sliding/full/kv-shared decode",
                          "prefill": "chunked prefill over cached prefix",
                          "hprefill": "gemma-style hybrid sliding/full/kv-shared chunked prefill",
+                         "mixedstep": "continuous-batching step: decode rows + a prefill chunk in one call",
                          "tiny": "tiny fp32 decode"}[args.workload],
             "batch": int(wsz), "num_q_heads": wl.hq, "num_kv_heads": wl.hkv, "head_dim": wl.head_dim,
             "block_size": wl.block_size, "max_seq_len": wl.max_seq_len,
@@ -445,6 +533,10 @@ def main():
         "kernels": kernels,
         "timing": timing,
     }
+    result.update(extra)
+    if mixed_step:
+        result["config"]["decode_rows"] = wl.num_decode
+        result["config"]["chunk_tokens"] = [int(c) for c in wl.chunk_lens[wl.num_decode:]]
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(wl, args)

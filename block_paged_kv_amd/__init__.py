@@ -69,6 +69,10 @@ _SIGNATURES = {
     + [_c_int32] * 3 + [_c_void_p, _c_size, _c_void_p],
     "paged_attn_prefill_chunk_fp8": [_c_void_p] * 5 + [_c_int32, _c_void_p, _c_void_p] + [_c_int32] * 8
     + [_c_float] * 3 + [_c_int32, _c_void_p],
+    "paged_attn_mixed": [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int32, _c_void_p,
+                         _c_void_p, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
+                         _c_int32, _c_int32, _c_int32, _c_float, _c_float, _c_float, _c_int32,
+                         _c_int32, _c_int32, _c_void_p, _c_size, _c_int32, _c_void_p],
     "paged_attn_decode_partition_tokens": [_c_int32] * 8 + [_P_I32],
     "paged_attn_decode_workspace_bytes": [_c_int32] * 9 + [ctypes.POINTER(_c_size)],
     "paged_attn_decode": [_c_void_p] * 5 + [_c_int32, _c_void_p] + [_c_int32] * 6 + [_c_float]
@@ -294,6 +298,33 @@ def paged_attn_prefill_chunk(out, q, k_pool, v_pool, block_tables, cu_q_lens, se
         _dev(cu_q_lens, "cu_q_lens", torch.int32, 1), _dev(seq_lens, "seq_lens", torch.int32, 1),
         B, T, int(max_q_len), hq, hkv, d, bs, nb, float(scale), int(sliding_window),
         _dtype_code(q), _stream(stream)), prepare)
+
+
+def paged_attn_mixed(out, q, k_pool, v_pool, block_tables, cu_q_lens, seq_lens, num_decode_rows,
+                     max_q_len, scale, max_seq_len, sliding_window=0, partition_tokens=0,
+                     workspace=None, k_scale=1.0, v_scale=1.0, stream=None, prepare=False):
+    """One continuous-batching step: rows ``[0, num_decode_rows)`` are decode rows
+    (one query each), the rest prefill chunks; ``out, q [T, Hq, D]`` bf16, pools bf16
+    or float8_e4m3fn (then ``k_scale``/``v_scale``). ``workspace`` as for
+    ``paged_attn_decode`` over the decode rows."""
+    torch = _torch()
+    nb, hkv, bs, d = _pool_geom(k_pool, v_pool)
+    T, hq, dq = (int(x) for x in q.shape)
+    B = int(seq_lens.shape[0])
+    if q.dtype != torch.bfloat16 or out.dtype != q.dtype or dq != d or tuple(out.shape) != (T, hq, d):
+        raise PagedError(PAGED_ERR_INVALID_ARG, "q/out must be [T, Hq, D] bf16")
+    if tuple(cu_q_lens.shape) != (B + 1,) or block_tables.dim() != 2 or int(block_tables.shape[0]) != B:
+        raise PagedError(PAGED_ERR_INVALID_ARG, "cu_q_lens must be [B+1] and block_tables [B, MB]")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    return _invoke(lib.paged_attn_mixed, (
+        _dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+        _dev(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
+        _dev(cu_q_lens, "cu_q_lens", torch.int32, 1), _dev(seq_lens, "seq_lens", torch.int32, 1),
+        B, int(num_decode_rows), T, int(max_q_len), hq, hkv, d, bs, nb, float(scale), float(k_scale),
+        float(v_scale), int(sliding_window), int(partition_tokens), int(max_seq_len), ws_ptr, ws_bytes,
+        _dtype_code(k_pool), _stream(stream)), prepare)
 
 
 # ------------------------------------------------------------------ FP8 KV pools

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libpagedkv.so")
 
-HIP_SOURCES = ["runtime.hip", "kv_copy.hip", "decode.hip", "prefill.hip"]
+HIP_SOURCES = ["runtime.hip", "kv_copy.hip", "decode.hip", "prefill.hip", "mixed.hip"]
 CXX_SOURCES = ["status.cpp", "allocator.cpp"]
 
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")

@@ -29,6 +29,7 @@
 
 #include <cmath>
 
+#include "attn.h"
 #include "device.h"
 #include "runtime.h"
 
@@ -1119,10 +1120,9 @@ extern "C" int32_t paged_attn_decode_workspace_bytes(int32_t batch, int32_t num_
 }
 
 namespace pagedkv {
-namespace {
 
-// Shared by the bf16/fp32 and the FP8 entry points. esz: pool element bytes
-// (q/out are bf16 when esz == 1).
+// Shared by the bf16/fp32 and the FP8 entry points and the mixed step. esz:
+// pool element bytes (q/out are bf16 when esz == 1).
 int32_t decode_impl(void* out, const void* q, const void* k_pool, const void* v_pool,
                     const int32_t* block_tables, int32_t max_blocks_per_seq,
                     const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
@@ -1208,7 +1208,6 @@ int32_t decode_impl(void* out, const void* q, const void* k_pool, const void* v_
   return ok();
 }
 
-}  // namespace
 }  // namespace pagedkv
 
 extern "C" int32_t paged_attn_decode(void* out, const void* q, const void* k_pool,

@@ -26,6 +26,7 @@
 #include <cmath>
 #include <type_traits>
 
+#include "attn.h"
 #include "device.h"
 #include "runtime.h"
 
@@ -385,9 +386,9 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillParams a
 using namespace pagedkv;
 
 namespace pagedkv {
-namespace {
 
-// Shared by the bf16 and FP8 entry points; esz: pool element bytes (q/out bf16).
+// Shared by the bf16 and FP8 entry points and the mixed step; esz: pool
+// element bytes (q/out bf16).
 int32_t prefill_impl(void* out, const void* q, const void* k_pool, const void* v_pool,
                      const int32_t* block_tables, int32_t max_blocks_per_seq,
                      const int32_t* cu_q_lens, const int32_t* seq_lens, int32_t batch,
@@ -460,7 +461,6 @@ int32_t prefill_impl(void* out, const void* q, const void* k_pool, const void* v
   return check_launch("paged_attn_prefill_chunk");
 }
 
-}  // namespace
 }  // namespace pagedkv
 
 extern "C" int32_t paged_attn_prefill_chunk(void* out, const void* q, const void* k_pool,

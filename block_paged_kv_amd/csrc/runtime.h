@@ -29,6 +29,32 @@ class LaunchTrace {
   hipEvent_t stop_ = nullptr;
 };
 
+// A second queue per device, for the part of one call that may run beside
+// the part on the caller's stream. Construction makes the side stream wait
+// for everything already enqueued on `s` (an event recorded on `s`); join()
+// makes `s` wait for everything enqueued on the side stream since (the
+// destructor joins too). The device's lock is held from construction to
+// join, so calls from several host threads do not interleave their event
+// records. The stream and its two events are created on the first use on a
+// device (outside graph capture) and kept until the process ends; the stream
+// has the default priority.
+class SideStream {
+ public:
+  explicit SideStream(hipStream_t s);
+  ~SideStream() { join(); }
+  SideStream(const SideStream&) = delete;
+  SideStream& operator=(const SideStream&) = delete;
+  int32_t status() const { return status_; }  // PAGED_OK once forked
+  hipStream_t get() const;
+  int32_t join();
+
+ private:
+  hipStream_t s_;
+  void* dev_ = nullptr;  // per-device state (runtime.hip)
+  bool locked_ = false;
+  int32_t status_ = PAGED_ERR_HIP;
+};
+
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 inline int esize_of(int32_t dtype) {

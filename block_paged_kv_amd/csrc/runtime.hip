@@ -78,6 +78,69 @@ void LaunchTrace::finish() {
   start_ = stop_ = nullptr;
 }
 
+namespace {
+
+struct DeviceSide {
+  std::mutex mu;
+  hipStream_t stream = nullptr;
+  hipEvent_t fork_ev = nullptr;
+  hipEvent_t join_ev = nullptr;
+};
+
+std::mutex g_side_mu;
+std::vector<DeviceSide*> g_side;  // per device id; never destroyed (the stream outlives static teardown)
+
+DeviceSide* side_state() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return nullptr;
+  std::lock_guard<std::mutex> lk(g_side_mu);
+  if (static_cast<int>(g_side.size()) <= dev) g_side.resize(dev + 1, nullptr);
+  if (!g_side[dev]) {
+    auto* d = new DeviceSide();
+    if (hipStreamCreateWithFlags(&d->stream, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&d->fork_ev, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&d->join_ev, hipEventDisableTiming) != hipSuccess) {
+      delete d;  // partially created handles are left to the process end
+      return nullptr;
+    }
+    g_side[dev] = d;
+  }
+  return g_side[dev];
+}
+
+}  // namespace
+
+SideStream::SideStream(hipStream_t s) : s_(s) {
+  DeviceSide* d = side_state();
+  if (!d) {
+    status_ = fail(PAGED_ERR_HIP, "cannot create the side stream");
+    return;
+  }
+  d->mu.lock();
+  dev_ = d;
+  locked_ = true;
+  if (hipEventRecord(d->fork_ev, s) != hipSuccess || hipStreamWaitEvent(d->stream, d->fork_ev, 0) != hipSuccess) {
+    status_ = fail(PAGED_ERR_HIP, "cannot order the side stream after the caller's stream");
+    d->mu.unlock();
+    locked_ = false;
+    return;
+  }
+  status_ = PAGED_OK;
+}
+
+hipStream_t SideStream::get() const { return static_cast<DeviceSide*>(dev_)->stream; }
+
+int32_t SideStream::join() {
+  if (!locked_) return PAGED_OK;
+  auto* d = static_cast<DeviceSide*>(dev_);
+  int32_t rc = PAGED_OK;
+  if (hipEventRecord(d->join_ev, d->stream) != hipSuccess || hipStreamWaitEvent(s_, d->join_ev, 0) != hipSuccess)
+    rc = fail(PAGED_ERR_HIP, "cannot order the caller's stream after the side stream");
+  d->mu.unlock();
+  locked_ = false;
+  return rc;
+}
+
 int32_t check_launch(const char* what) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PAGED_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));

@@ -242,6 +242,40 @@ int32_t paged_attn_prefill_chunk_fp8(void* out, const void* q, const void* k_poo
                                      float scale, float k_scale, float v_scale,
                                      int32_t sliding_window, void* stream);
 
+/* One continuous-batching step over one layer (batching-perf-path doc,
+ * current state: chunked prefill of joining requests interleaved with the
+ * running decode rows). Rows [0, num_decode_rows) are decode rows with one
+ * query each (cu_q_lens[b] == b for b <= num_decode_rows: query b is row b's
+ * newest position); rows [num_decode_rows, batch) are prefill chunks. The
+ * result is exactly that of paged_attn_prefill_chunk over all rows (a decode
+ * row is a chunk of one); the decode rows run through the split-K decode
+ * kernels on `stream`, the chunk rows through the prefill kernel on a second
+ * stream the library keeps per device, so both run at once; `stream` waits
+ * for both before anything enqueued after the call. The first call on a
+ * device creates that stream and two events (keep it outside graph capture);
+ * afterwards calls are capturable.
+ *   out, q         : device bf16, [total_q][num_q_heads][head_dim]
+ *   k_pool, v_pool : device, kv_dtype PAGED_BF16 (k_scale = v_scale = 1) or
+ *                    PAGED_FP8_E4M3 (values k_scale * code, v_scale * code)
+ *   block_tables   : device int32 [batch][max_blocks_per_seq]
+ *   cu_q_lens      : device int32 [batch + 1], as for paged_attn_prefill_chunk
+ *   seq_lens       : device int32 [batch]; decode rows' at most max_seq_len
+ *   max_q_len      : bound on the chunk rows' query counts
+ *   partition_tokens, max_seq_len, workspace: as for paged_attn_decode with
+ *                    batch = num_decode_rows (size the workspace with
+ *                    paged_attn_decode_workspace_bytes(num_decode_rows, ...))
+ *   head_dim       : 64, 128 or 256 when any chunk row is present
+ * Errors: those of both entry points, checked before anything is enqueued. */
+int32_t paged_attn_mixed(void* out, const void* q, const void* k_pool, const void* v_pool,
+                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* cu_q_lens, const int32_t* seq_lens, int32_t batch,
+                         int32_t num_decode_rows, int32_t total_q, int32_t max_q_len,
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t num_blocks, float scale, float k_scale,
+                         float v_scale, int32_t sliding_window, int32_t partition_tokens,
+                         int32_t max_seq_len, void* workspace, size_t workspace_bytes,
+                         int32_t kv_dtype, void* stream);
+
 /* ----------------------------------------------------------------------
  * Kernel timing (HIP events around every launch, on the launch's stream)
  * -------------------------------------------------------------------- */

@@ -90,18 +90,26 @@ def gpu_setup(wl, tabs, fill=float("nan"), device="cuda"):
     return dev
 
 
+def decode_max_seq_len(wl):
+    """Longest context among the rows that run as decode rows."""
+    if wl.kind == "decode":
+        return wl.max_seq_len
+    return int(wl.seq_lens[:wl.num_decode].max()) if wl.num_decode else 0
+
+
 def gpu_workspace(wl, dev, partition_tokens=None, max_seq_len=None):
     """One uint8 workspace large enough for every decode layer of the step."""
     import torch
 
     import block_paged_kv_amd as pk
 
-    if wl.kind != "decode":
+    if wl.kind != "decode" and not wl.num_decode:
         return None
     part = wl.partition_tokens if partition_tokens is None else partition_tokens
-    msl = wl.max_seq_len if max_seq_len is None else max_seq_len
+    rows = wl.batch if wl.kind == "decode" else wl.num_decode
+    msl = decode_max_seq_len(wl) if max_seq_len is None else max_seq_len
     dt = "fp8" if wl.kv_dtype == "fp8" else wl.dtype
-    need = max(pk.paged_attn_decode_workspace_bytes(wl.batch, wl.hq, wl.hkv, wl.head_dim,
+    need = max(pk.paged_attn_decode_workspace_bytes(rows, wl.hq, wl.hkv, wl.head_dim,
                                                     wl.block_size, msl, L.window, part, dt)
                for L in wl.layers)
     return torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
@@ -128,10 +136,15 @@ def gpu_step(wl, dev, outs=None, workspace=None, partition_tokens=None, max_seq_
         else:
             pk.paged_kv_write(d["k_pool"], d["v_pool"], d["step_k"], d["step_v"], d["step_slots"])
     part = wl.partition_tokens if partition_tokens is None else partition_tokens
-    msl = wl.max_seq_len if max_seq_len is None else max_seq_len
+    msl = decode_max_seq_len(wl) if max_seq_len is None else max_seq_len
     for n in names:
         d = dev[n]
-        if wl.kind == "decode":
+        if wl.kind == "prefill" and wl.num_decode:
+            pk.paged_attn_mixed(outs[n], d["q"], d["k_pool"], d["v_pool"], d["tables"], dev["_cu_q"],
+                                dev["_seq_lens"], wl.num_decode, int(wl.chunk_lens.max()), wl.scale, msl,
+                                sliding_window=d["window"], partition_tokens=part, workspace=workspace,
+                                k_scale=d["k_scale"], v_scale=d["v_scale"])
+        elif wl.kind == "decode":
             if fp8:
                 pk.paged_attn_decode_fp8(outs[n], d["q"], d["k_pool"], d["v_pool"], d["tables"],
                                          dev["_seq_lens"], wl.scale, d["k_scale"], d["v_scale"], msl,

@@ -30,6 +30,11 @@ rounded to bf16 with round-to-nearest-even for bf16 workloads):
                  own 1024-block pool and null entries for expired blocks, full
                  attention, and a KV-shared layer reading the full layer's pool
                  and tables, which writes nothing).
+* ``mixedstep`` -- one continuous-batching step: 32 decode rows (contexts uniform
+                 in [128, 8192], one new token each, 512-token split-K
+                 partitions) and one joining request whose 2048-token chunk
+                 follows a 6144-token cached prefix; Hq=32, Hkv=8, D=128, bf16,
+                 a 32768-block pool. Rows with one query come first.
 
 Random draw order per workload (``numpy.random.default_rng(seed)``): the
 allocator free-list permutation, then lengths and prefix choices, then the
@@ -44,7 +49,8 @@ from dataclasses import dataclass, field
 import numpy as np
 
 BLOCK_SIZE = 16
-SEEDS = {"tiny": 1000, "qwen3": 1001, "mixed": 1002, "hybrid": 1003, "prefill": 1004, "hprefill": 1005}
+SEEDS = {"tiny": 1000, "qwen3": 1001, "mixed": 1002, "hybrid": 1003, "prefill": 1004, "hprefill": 1005,
+         "mixedstep": 1006}
 
 
 def round_bf16(x):
@@ -90,6 +96,7 @@ class Workload:
     domain: int = 0
     wave_size: int = 0        # rows per benchmark step when several batches share a pool
     kv_dtype: str = ""        # "" = the pools hold ``dtype``; "fp8" = E4M3 codes with per-layer scales
+    num_decode: int = 0       # prefill kind: leading rows that are decode rows (one query each)
 
     @property
     def max_seq_len(self):
@@ -232,6 +239,33 @@ def _make(name, rng, bs, *, batch=None, hq=None, hkv=None, head_dim=None, contex
             layer.v[b] = np.concatenate([layer.v[b], _normal(rng, (int(C[b]), Hkv, D), True)])
         return Workload(name, "prefill", B, Hq, Hkv, D, "bf16", lens, toks, [layer],
                         1.0 / math.sqrt(D), chunk_lens=C, block_size=bs)
+
+    if name == "mixedstep":
+        ND, Hq, Hkv, D = 32 if batch is None else batch, hq or 32, hkv or 8, head_dim or 128
+        NB = num_blocks or 32768
+        free = rng.permutation(np.arange(1, NB)).astype(np.int32)
+        lo, hi = context if context is not None else (128, 8192)
+        dec = rng.integers(lo, hi + 1, size=ND).astype(np.int32)
+        Cp = np.array(chunk if chunk is not None else [2048], dtype=np.int32).reshape(-1)
+        Pp = np.array(prefix if prefix is not None else [6144] * len(Cp), dtype=np.int32).reshape(-1)
+        C = np.concatenate([np.ones(ND, np.int32), Cp]).astype(np.int32)
+        P = np.concatenate([dec - 1, Pp]).astype(np.int32)
+        lens = (P + C).astype(np.int32)
+        B = len(C)
+        layer = Layer("main", NB, window or 0, None, free)
+        toks = []
+        for b in range(B):
+            layer.k.append(_normal(rng, (int(P[b]), Hkv, D), True))
+            layer.v.append(_normal(rng, (int(P[b]), Hkv, D), True))
+            layer.live_from.append(0)
+            toks.append(_suffix_tokens(b, int(lens[b])))
+        layer.q = _normal(rng, (int(C.sum()), Hq, D), True)
+        for b in range(B):  # the step's new tokens: one per decode row, the chunk
+            layer.k[b] = np.concatenate([layer.k[b], _normal(rng, (int(C[b]), Hkv, D), True)])
+            layer.v[b] = np.concatenate([layer.v[b], _normal(rng, (int(C[b]), Hkv, D), True)])
+        return Workload(name, "prefill", B, Hq, Hkv, D, "bf16", lens, toks, [layer],
+                        1.0 / math.sqrt(D), partition_tokens=512 if part is None else part,
+                        chunk_lens=C, block_size=bs, num_decode=ND)
 
     if name == "hprefill":
         B, Hq, Hkv, D = batch or 4, hq or 8, hkv or 1, head_dim or 256

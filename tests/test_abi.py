@@ -121,6 +121,25 @@ def test_head_dim_512_limits():
         pk.PAGED_ERR_INVALID_ARG
 
 
+def test_mixed_step_argument_errors():
+    L = pk.lib
+
+    def call(B=3, nd=2, T=10, d=128, dt=pk.PAGED_BF16, ks=1.0, vs=1.0, part=64, ws=None, wsb=0, ptr=None):
+        return L.paged_attn_mixed(ptr, ptr, ptr, ptr, ptr, 4, ptr, ptr, B, nd, T, 8, 8, 8, d, 16, 8, 0.1, ks, vs,
+                                  0, part, 64, ws, wsb, dt, None)
+
+    assert call(dt=pk.PAGED_F32) == pk.PAGED_ERR_DTYPE
+    assert call(nd=4) == pk.PAGED_ERR_INVALID_ARG           # more decode rows than rows
+    assert call(T=1) == pk.PAGED_ERR_INVALID_ARG            # fewer queries than decode rows
+    assert call(ks=2.0) == pk.PAGED_ERR_INVALID_ARG         # scales belong to FP8 pools
+    assert call(B=0, nd=0, T=0) == pk.PAGED_OK              # nothing to do
+    assert call() == pk.PAGED_ERR_INVALID_ARG               # NULL pointers
+    # everything below is rejected before any device call
+    assert call(d=512, ptr=16) == pk.PAGED_ERR_INVALID_ARG  # chunk rows need head_dim <= 256
+    assert call(ptr=16, part=32) == pk.PAGED_ERR_CAPACITY   # two partitions: a workspace is needed
+    assert b"workspace" in pk.lib.paged_last_error()
+
+
 def test_library_rule_needs_a_device_here():
     # No GPU in this container: the rule's device query fails cleanly.
     with pytest.raises(pk.PagedError) as e:

@@ -360,6 +360,39 @@ def test_hybrid_prefill_full_size_sampled_rows(pk):
     run_case(pk, wl, rows=rows, label="hprefill-full")
 
 
+# One continuous-batching step: decode rows (split-K decode kernels on the
+# caller's stream) and prefill chunks (prefill kernel on the side stream) in
+# one call, checked against the oracle's varlen prefill over all rows.
+MIXED_STEP = [
+    dict(batch=5, context=(20, 900), chunk=[150, 64], prefix=[300, 0], num_blocks=200, part=128),
+    dict(batch=3, context=(1, 300), chunk=[1, 200], prefix=[40, 33], num_blocks=100, part=0),
+    dict(batch=4, context=(100, 600), chunk=[77], prefix=[500], num_blocks=200, window=100, part=64),
+    dict(batch=6, context=(1, 400), chunk=[33, 129], prefix=[64, 17], num_blocks=300, block_size=8, part=64),
+    dict(batch=2, context=(300, 700), chunk=[100], prefix=[250], num_blocks=100, block_size=64, hq=8, hkv=1,
+         head_dim=256, part=128),
+    dict(batch=0, chunk=[120, 5], prefix=[30, 300], num_blocks=100),
+    dict(batch=4, context=(10, 200), chunk=[], prefix=[], num_blocks=100, part=32),
+]
+
+
+@pytest.mark.parametrize("kw", MIXED_STEP, ids=[str(i) for i in range(len(MIXED_STEP))])
+def test_mixed_step_small(pk, kw):
+    run_case(pk, synth.make("mixedstep", **kw), label="mixed-step")
+
+
+def test_mixed_step_fp8(pk):
+    run_case(pk, synth.make("mixedstep", batch=5, context=(20, 900), chunk=[150, 64], prefix=[300, 0],
+                            num_blocks=200, part=128, kv_dtype="fp8"), label="mixed-step-fp8")
+
+
+def test_mixed_step_full_size_sampled_rows(pk):
+    wl = synth.make("mixedstep")
+    T = int(wl.chunk_lens.sum())
+    rows = sorted(set(list(range(wl.num_decode)) + [wl.num_decode, wl.num_decode + 1, T - 2, T - 1] +
+                      list(np.random.default_rng(7).integers(wl.num_decode, T, size=30))))
+    run_case(pk, wl, rows=rows, label="mixed-step-full")
+
+
 def test_prefill_chunk_of_one_matches_decode(pk):
     import torch
 
@@ -379,6 +412,8 @@ def test_prefill_chunk_of_one_matches_decode(pk):
 @pytest.mark.parametrize("name,kw", [
     ("qwen3", dict(context=300, prefix=64, num_blocks=200)),
     ("prefill", dict(batch=2, context=[300, 64], chunk=[150, 100], num_blocks=64)),
+    ("mixedstep", dict(batch=5, context=(20, 900), chunk=[150, 64], prefix=[300, 0], num_blocks=200,
+                       part=128)),
 ])
 def test_step_graph_replays_match_eager(pk, name, kw):
     """The step (KV write + attention) captured in a HIP graph, with the
@@ -400,6 +435,12 @@ def test_step_graph_replays_match_eager(pk, name, kw):
     if wl.kind == "decode":
         calls.append(pk.paged_attn_decode(out, d["q"], d["k_pool"], d["v_pool"], d["tables"], dev["_seq_lens"],
                                           wl.scale, wl.max_seq_len, workspace=ws, stream=s, prepare=True))
+    elif wl.num_decode:
+        # decode rows on `s`, chunk rows on the library's side stream, joined into `s`
+        calls.append(pk.paged_attn_mixed(out, d["q"], d["k_pool"], d["v_pool"], d["tables"], dev["_cu_q"],
+                                         dev["_seq_lens"], wl.num_decode, int(wl.chunk_lens.max()), wl.scale,
+                                         runner.decode_max_seq_len(wl), partition_tokens=wl.partition_tokens,
+                                         workspace=ws, stream=s, prepare=True))
     else:
         calls.append(pk.paged_attn_prefill_chunk(out, d["q"], d["k_pool"], d["v_pool"], d["tables"], dev["_cu_q"],
                                                  dev["_seq_lens"], int(wl.chunk_lens.max()), wl.scale,
