@@ -413,36 +413,6 @@ __device__ __forceinline__ floatx4_t mfma_k16(const uint2& a, const uint2& b, fl
                                                    __builtin_bit_cast(shortx4d_t, b), c, 0, 0, 0);
 }
 
-// 16 zero bytes in the code object: the load source of token rows a stage
-// does not attend, so those LDS rows hold finite zeros.
-__device__ __attribute__((aligned(16))) const uint4 kZeroChunk = {0u, 0u, 0u, 0u};
-
-// global_load_lds_dwordx4: each lane copies 16 bytes from global memory to
-// LDS byte offset m0 + 16 * lane (m0 wave-uniform). Issued as assembly so that
-// the compiler leaves the vector-memory counter to the stage pipeline below
-// (it would otherwise drain every outstanding load before each LDS read).
-// Two address forms: a 64-bit address per lane, or a wave-uniform 64-bit base
-// (held in scalar registers) plus a 32-bit byte offset per lane.
-__device__ __forceinline__ void lds_dma16(const void* gaddr, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :: "s"(m0), "v"(gaddr) : "memory", "m0");
-}
-__device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :: "s"(m0), "v"(voff), "s"(base) : "memory", "m0");
-}
-
-// LDS byte offset of a __shared__ location: the low half of its generic
-// address (the high half is the LDS aperture).
-__device__ __forceinline__ uint32_t lds_offset(const void* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
-}
-
-// Wait until at most N vector-memory operations of this wave are in flight.
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
-}
 
 template <int D, int ESZ>
 __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_lds_kernel(DecodeParams a) {

@@ -66,19 +66,25 @@ __device__ __forceinline__ floatx4_t mfma16x16x32(const uint4& a, const uint4& b
 // exactly as they are staged, so everything after staging is shared).
 template <int D, int ESZ>
 __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillParams a) {
-  // LDS row strides (elements): rows padded by 32 bytes. Measured on gfx950
-  // with the two read patterns below (K: 16 rows x 64 bytes per ds_read_b128;
-  // V: 16 rows x 32 bytes per ds_read_b64_tr_b16), a 32-byte pad is the
-  // fastest of the paddings from 0 to 128 bytes for both.
-  constexpr int KSTR = D + 16;
-  constexpr int VSTR = D + 16;
+  // LDS tiles: key rows of D bf16 elements, unpadded; the 16-byte chunks of
+  // a row are stored XOR-swizzled (chunk c of row r at position c ^ swz(r))
+  // so that both read patterns below are free of bank conflicts: K reads 16
+  // rows x one 16-byte chunk per ds_read_b128 (swz_k: a distinct position
+  // per row of a 16-row group), V reads 8 rows x 32 contiguous bytes per
+  // half-wave ds_read_b64_tr_b16 (swz_v: even values, so a row's chunk pair
+  // stays together and the 8 rows' pairs are distinct). With 128-byte rows
+  // (head_dim 64) two rows share a bank line and the row's low bit is
+  // folded out.
   constexpr int DCH = D / 8;         // 16-byte chunks per key row
   constexpr int KS = D / 32;         // MFMA k-steps over head_dim
   constexpr int NT = D / 16;         // output column tiles
+  constexpr int ROWB = D * 2;        // bytes per LDS key row
   constexpr float kNegInf = -INFINITY;
+  auto swz_k = [](int r) { return D >= 128 ? (r & 15) : ((r >> 1) & 7); };
+  auto swz_v = [](int r) { return D >= 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); };
 
-  __shared__ __attribute__((aligned(16))) uint16_t k_s[2][kTileN * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t v_s[2][kTileN * VSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t k_s[2][kTileN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t v_s[2][kTileN * D];
 
   // XCD-aware work mapping: XCD x takes work items [x*per_xcd, (x+1)*per_xcd).
   const int lin = blockIdx.x;
@@ -104,7 +110,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillParams a
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lq = lane & 15;   // query column inside a 16-wide tile
   const int lg = lane >> 4;   // lane group 0..3
 
@@ -156,72 +162,102 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillParams a
   };
   auto phys_ok = [&](int phys) { return phys > 0 && phys < a.nb; };
 
-  // Staging (global -> registers -> LDS, double buffered): wave w moves keys
-  // 16w .. 16w+15 of a tile; lane l copies 16-byte chunk l % DCH of keys
-  // 16w + (64/DCH)*i + l / DCH, for K and for V alike. Both stay row-major in
-  // LDS: the P.V operand is read with ds_read_b64_tr_b16, which hands each
-  // lane four consecutive keys of one head_dim column.
+  // Staging (double buffered): wave w moves keys 16w .. 16w+15 of a tile, K
+  // and V alike. bf16 pools go straight to LDS (global_load_lds_dwordx4: one
+  // instruction fills 1 KiB, i.e. RPI consecutive key rows; each lane names
+  // the global chunk that belongs at its swizzled LDS position), so no
+  // registers hold the next tile. FP8 pools are read into registers, widened
+  // to bf16 and stored at the same swizzled positions.
   // The wave's 16 keys lie in one block (block_size >= 16) or in two
   // (block_size 8, keys 8..15 in the second): block ids come from the tile's
   // entries by readlane, so block bases are wave-uniform and each lane adds a
   // loop-invariant 32-bit offset.
-  constexpr int KROWS = 64 / DCH;                 // keys one load instruction covers
-  constexpr int KI = 16 / KROWS;                  // loads per lane per tile (K, and V)
-  uint4 kreg[KI], vreg[KI];
-  const int k_key = wave * 16 + lane / DCH;       // + KROWS * i
-  const int k_dc = lane % DCH;
+  constexpr int RPI = 64 / DCH;                   // key rows per load instruction
+  constexpr int KI = 16 / RPI;                    // load instructions per wave per tile (K, and V)
   const bool bs8 = bs_log2 == 3;
-  uint32_t lane_off[KI];
+  const int lrow = lane / DCH;                    // row inside the instruction
+  const int lch = lane % DCH;                     // LDS chunk position inside the row
+  uint32_t koff[KI], voff[KI];                    // byte offsets inside the wave's block(s)
 #pragma unroll
-  for (int i = 0; i < KI; ++i)
-    lane_off[i] = static_cast<uint32_t>(((lane / DCH + KROWS * i) & (bs8 ? 7 : 15)) * D + k_dc * 8);
-  // Eight head_dim elements of one key row as bf16 (16 bytes): read as they
-  // are (bf16) or widened from eight E4M3 codes.
-  auto load_row_chunk = [&](const void* pool, size_t elem) -> uint4 {
-    if constexpr (ESZ == 1)
-      return widen_e4m3x8(*reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(pool) + elem));
-    else
-      return *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(pool) + elem);
-  };
-  auto stage_load = [&](int kt, int ent) {
+  for (int i = 0; i < KI; ++i) {
+    const int r = RPI * i + lrow;                 // key row inside the wave's 16 (swz depends on r % 16)
+    const int in_blk = r & (bs8 ? 7 : 15);
+    koff[i] = static_cast<uint32_t>((in_blk * D + (lch ^ swz_k(r)) * 8) * ESZ);
+    voff[i] = static_cast<uint32_t>((in_blk * D + (lch ^ swz_v(r)) * 8) * ESZ);
+  }
+  uint2 kraw[ESZ == 1 ? KI : 1], vraw[ESZ == 1 ? KI : 1];  // FP8: codes awaiting their widening store
+  const char* kpool = static_cast<const char*>(a.k_pool);
+  const char* vpool = static_cast<const char*>(a.v_pool);
+  auto stage_load = [&](int kt, int ent, int buf) {
     const int ts = kt * kTileN;
     const int e0 = (wave * 16) >> bs_log2;
     const int phys_lo = __builtin_amdgcn_readlane(ent, e0);
     const int phys_hi = __builtin_amdgcn_readlane(ent, bs8 ? e0 + 1 : e0);
-    // Element offset of the wave's first key inside its block (0 unless block_size > 16).
+    // Byte offset of the wave's first key row inside its block (0 unless block_size > 16).
     const size_t sub = static_cast<size_t>((ts + wave * 16) & bs_mask) * D;
-    const size_t base_lo = ((static_cast<size_t>(phys_lo) * a.hkv + kvh) << bs_log2) * D + sub;
-    const size_t base_hi = ((static_cast<size_t>(phys_hi) * a.hkv + kvh) << bs_log2) * D + sub;
-    if (ts + kTileN <= n && phys_ok(phys_lo) && phys_ok(phys_hi)) {
-      // Every key of the tile exists and every block id is valid.
+    const size_t base_lo = (((static_cast<size_t>(phys_lo) * a.hkv + kvh) << bs_log2) * D + sub) * ESZ;
+    const size_t base_hi = (((static_cast<size_t>(phys_hi) * a.hkv + kvh) << bs_log2) * D + sub) * ESZ;
+    const bool full = ts + kTileN <= n && phys_ok(phys_lo) && phys_ok(phys_hi);
+    if constexpr (ESZ == 2) {
+      const uint32_t kl = lds_offset(&k_s[buf][0]) + wave * 16 * ROWB;
+      const uint32_t vl = lds_offset(&v_s[buf][0]) + wave * 16 * ROWB;
+      // The buffer's previous tile was read before the last barrier; this
+      // wave's own reads of it have returned too.
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (full) {
+        // Every key of the tile exists and every block id is valid.
 #pragma unroll
-      for (int i = 0; i < KI; ++i) {
-        const size_t base = (bs8 && KROWS * i >= 8) ? base_hi : base_lo;
-        kreg[i] = load_row_chunk(a.k_pool, base + lane_off[i]);
-        vreg[i] = load_row_chunk(a.v_pool, base + lane_off[i]);
+        for (int i = 0; i < KI; ++i) {
+          const size_t base = (bs8 && RPI * i >= 8) ? base_hi : base_lo;
+          lds_dma16(kpool + base, koff[i], kl + i * 1024);
+          lds_dma16(vpool + base, voff[i], vl + i * 1024);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < KI; ++i) {
+          const int r = RPI * i + lrow;
+          const bool hi = bs8 && r >= 8;
+          const bool ok = ts + wave * 16 + r < n && phys_ok(hi ? phys_hi : phys_lo);
+          const size_t base = hi ? base_hi : base_lo;
+          lds_dma16(ok ? static_cast<const void*>(kpool + base + koff[i]) : &kZeroChunk, kl + i * 1024);
+          lds_dma16(ok ? static_cast<const void*>(vpool + base + voff[i]) : &kZeroChunk, vl + i * 1024);
+        }
       }
     } else {
+      // Every load is issued before any is used; absent rows read the zero chunk.
+      if (full) {
 #pragma unroll
-      for (int i = 0; i < KI; ++i) {
-        const bool hi = bs8 && KROWS * i >= 8;
-        const int phys = hi ? phys_hi : phys_lo;
-        const size_t base = hi ? base_hi : base_lo;
-        if (ts + k_key + KROWS * i < n && phys_ok(phys)) {
-          kreg[i] = load_row_chunk(a.k_pool, base + lane_off[i]);
-          vreg[i] = load_row_chunk(a.v_pool, base + lane_off[i]);
-        } else {
-          kreg[i] = make_uint4(0, 0, 0, 0);
-          vreg[i] = make_uint4(0, 0, 0, 0);
+        for (int i = 0; i < KI; ++i) {
+          const size_t base = (bs8 && RPI * i >= 8) ? base_hi : base_lo;
+          kraw[i] = *reinterpret_cast<const uint2*>(kpool + base + koff[i]);
+          vraw[i] = *reinterpret_cast<const uint2*>(vpool + base + voff[i]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < KI; ++i) {
+          const int r = RPI * i + lrow;
+          const bool hi = bs8 && r >= 8;
+          const bool ok = ts + wave * 16 + r < n && phys_ok(hi ? phys_hi : phys_lo);
+          const size_t base = hi ? base_hi : base_lo;
+          kraw[i] = *reinterpret_cast<const uint2*>(ok ? static_cast<const void*>(kpool + base + koff[i]) : &kZeroChunk);
+          vraw[i] = *reinterpret_cast<const uint2*>(ok ? static_cast<const void*>(vpool + base + voff[i]) : &kZeroChunk);
         }
       }
     }
   };
+  // Completes the staging of buffer `buf` for this wave: the direct loads
+  // have landed (bf16), or the widened registers are stored (FP8). A barrier
+  // must follow before any wave reads the tile.
   auto stage_store = [&](int buf) {
+    if constexpr (ESZ == 2) {
+      vm_wait<0>();
+    } else {
 #pragma unroll
-    for (int i = 0; i < KI; ++i) {
-      const int key = k_key + KROWS * i;
-      *reinterpret_cast<uint4*>(&k_s[buf][key * KSTR + k_dc * 8]) = kreg[i];
-      *reinterpret_cast<uint4*>(&v_s[buf][key * VSTR + k_dc * 8]) = vreg[i];
+      for (int i = 0; i < KI; ++i) {
+        const int row = wave * 16 + RPI * i + lrow;
+        *reinterpret_cast<uint4*>(&k_s[buf][row * D + lch * 8]) = widen_e4m3x8(kraw[i]);
+        *reinterpret_cast<uint4*>(&v_s[buf][row * D + lch * 8]) = widen_e4m3x8(vraw[i]);
+      }
     }
   };
 
@@ -242,7 +278,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillParams a
     for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const uint4 ka = *reinterpret_cast<const uint4*>(&ks_buf[(t4 * 16 + lq) * KSTR + ks * 32 + lg * 8]);
+        const uint4 ka = *reinterpret_cast<const uint4*>(&ks_buf[(t4 * 16 + lq) * D + (((4 * ks + lg) ^ swz_k(lq)) << 3)]);
 #pragma unroll
         for (int j = 0; j < 2; ++j) s[j][t4] = mfma16x16x32(ka, qreg[j][ks], s[j][t4]);
       }
@@ -328,11 +364,14 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillParams a
     for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) lsum[j] = mfma16x16x32(pa[j][kk], ones, lsum[j]);
-      const uint16_t* vbase = &vs_buf[(kk * 32 + 4 * lg + (lq >> 2)) * VSTR + 4 * (lq & 3)];
+      const int vrow = kk * 32 + 4 * lg + (lq >> 2);  // and vrow + 16: same swizzle
+      const uint16_t* vbase = &vs_buf[vrow * D + 4 * (lq & 1)];
+      const int vsw = swz_v(vrow);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const uint2 v0 = ds_read_tr16(vbase + nt * 16);
-        const uint2 v1 = ds_read_tr16(vbase + 16 * VSTR + nt * 16);
+        const int vc = ((2 * nt + ((lq & 3) >> 1)) ^ vsw) << 3;
+        const uint2 v0 = ds_read_tr16(vbase + vc);
+        const uint2 v1 = ds_read_tr16(vbase + 16 * D + vc);
         const uint4 vb = make_uint4(v0.x, v0.y, v1.x, v1.y);
 #pragma unroll
         for (int j = 0; j < 2; ++j) o[j][nt] = mfma16x16x32(pa[j][kk], vb, o[j][nt]);
@@ -341,15 +380,15 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillParams a
   };
 
   int ent_next = load_entries(kt_begin + 1);
-  stage_load(kt_begin, load_entries(kt_begin));
+  stage_load(kt_begin, load_entries(kt_begin), 0);
   stage_store(0);
   __syncthreads();
 
   for (int kt = kt_begin; kt <= kt_end; ++kt) {
     const int buf = (kt - kt_begin) & 1;
     const bool has_next = kt < kt_end;
-    if (has_next) {  // tile kt+1 streams into registers while tile kt computes
-      stage_load(kt + 1, ent_next);
+    if (has_next) {  // tile kt+1 streams into the other buffer while tile kt computes
+      stage_load(kt + 1, ent_next, buf ^ 1);
       ent_next = load_entries(kt + 2);
     }
     const int ts = kt * kTileN;
