@@ -33,10 +33,15 @@
 namespace pagedkv {
 namespace {
 
-constexpr int kWaves = 4;
 constexpr int kRowsPerWave = 32;
-constexpr int kTileM = kWaves * kRowsPerWave;  // 128 query rows per workgroup
 constexpr int kTileN = 64;                      // keys per K/V tile
+// Waves per workgroup: eight by default up to head_dim 128 (256 query rows
+// share each staged K/V tile; the workgroup fills a CU's registers), four at
+// head_dim 256, whose waves need more than 256 registers (one wave per SIMD;
+// the 128 KiB of tiles allow one workgroup), and four when decode
+// workgroups run beside the prefill (mixed step), so that a CU can hold one
+// of each.
+constexpr int default_waves(int d) { return d >= 256 ? 4 : 8; }
 constexpr int kNumXcd = 8;
 
 typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
@@ -50,7 +55,7 @@ struct PrefillParams {
   const int32_t* cu_q;
   const int32_t* seq_lens;
   int32_t mb, hq, hkv, group, bs_log2, nb, window;
-  int32_t tiles_per_head;   // ceil(max_q_len * group / kTileM)
+  int32_t tiles_per_head;   // ceil(max_q_len * group / query rows per workgroup)
   int32_t work_items;       // batch * hkv * tiles_per_head
   int32_t per_xcd;          // ceil(work_items / kNumXcd)
   float scale_log2;         // scale * log2(e) (times the K scale for FP8 pools)
@@ -64,8 +69,10 @@ __device__ __forceinline__ floatx4_t mfma16x16x32(const uint4& a, const uint4& b
 
 // ESZ: bytes per pool element (2: bf16; 1: FP8 E4M3 codes, widened to bf16
 // exactly as they are staged, so everything after staging is shared).
-template <int D, int ESZ>
-__global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillParams a) {
+template <int D, int ESZ, int NW>
+__global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill_kernel(PrefillParams a) {
+  constexpr int kWaves = NW;
+  constexpr int kTileM = NW * kRowsPerWave;
   // LDS tiles: key rows of D bf16 elements, unpadded; the 16-byte chunks of
   // a row are stored XOR-swizzled (chunk c of row r at position c ^ swz(r))
   // so that both read patterns below are free of bank conflicts: K reads 16
@@ -173,34 +180,37 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillParams a
   // entries by readlane, so block bases are wave-uniform and each lane adds a
   // loop-invariant 32-bit offset.
   constexpr int RPI = 64 / DCH;                   // key rows per load instruction
-  constexpr int KI = 16 / RPI;                    // load instructions per wave per tile (K, and V)
+  constexpr int KPW = kTileN / kWaves;            // keys each wave stages (16 or 8)
+  constexpr int KI = KPW / RPI;                   // load instructions per wave per tile (K, and V)
   const bool bs8 = bs_log2 == 3;
+  const bool split = bs8 && KPW > 8;              // the wave's keys span two blocks
   const int lrow = lane / DCH;                    // row inside the instruction
   const int lch = lane % DCH;                     // LDS chunk position inside the row
   uint32_t koff[KI], voff[KI];                    // byte offsets inside the wave's block(s)
 #pragma unroll
   for (int i = 0; i < KI; ++i) {
-    const int r = RPI * i + lrow;                 // key row inside the wave's 16 (swz depends on r % 16)
-    const int in_blk = r & (bs8 ? 7 : 15);
-    koff[i] = static_cast<uint32_t>((in_blk * D + (lch ^ swz_k(r)) * 8) * ESZ);
-    voff[i] = static_cast<uint32_t>((in_blk * D + (lch ^ swz_v(r)) * 8) * ESZ);
+    const int r = RPI * i + lrow;                 // key row among the wave's KPW
+    const int tr = wave * KPW + r;                // tile row (the swizzles use its low bits)
+    const int in_blk = split ? (r & 7) : r;
+    koff[i] = static_cast<uint32_t>((in_blk * D + (lch ^ swz_k(tr)) * 8) * ESZ);
+    voff[i] = static_cast<uint32_t>((in_blk * D + (lch ^ swz_v(tr)) * 8) * ESZ);
   }
   uint2 kraw[ESZ == 1 ? KI : 1], vraw[ESZ == 1 ? KI : 1];  // FP8: codes awaiting their widening store
   const char* kpool = static_cast<const char*>(a.k_pool);
   const char* vpool = static_cast<const char*>(a.v_pool);
   auto stage_load = [&](int kt, int ent, int buf) {
     const int ts = kt * kTileN;
-    const int e0 = (wave * 16) >> bs_log2;
+    const int e0 = (wave * KPW) >> bs_log2;
     const int phys_lo = __builtin_amdgcn_readlane(ent, e0);
-    const int phys_hi = __builtin_amdgcn_readlane(ent, bs8 ? e0 + 1 : e0);
+    const int phys_hi = __builtin_amdgcn_readlane(ent, split ? e0 + 1 : e0);
     // Byte offset of the wave's first key row inside its block (0 unless block_size > 16).
-    const size_t sub = static_cast<size_t>((ts + wave * 16) & bs_mask) * D;
+    const size_t sub = static_cast<size_t>((ts + wave * KPW) & bs_mask) * D;
     const size_t base_lo = (((static_cast<size_t>(phys_lo) * a.hkv + kvh) << bs_log2) * D + sub) * ESZ;
     const size_t base_hi = (((static_cast<size_t>(phys_hi) * a.hkv + kvh) << bs_log2) * D + sub) * ESZ;
     const bool full = ts + kTileN <= n && phys_ok(phys_lo) && phys_ok(phys_hi);
     if constexpr (ESZ == 2) {
-      const uint32_t kl = lds_offset(&k_s[buf][0]) + wave * 16 * ROWB;
-      const uint32_t vl = lds_offset(&v_s[buf][0]) + wave * 16 * ROWB;
+      const uint32_t kl = lds_offset(&k_s[buf][0]) + wave * KPW * ROWB;
+      const uint32_t vl = lds_offset(&v_s[buf][0]) + wave * KPW * ROWB;
       // The buffer's previous tile was read before the last barrier; this
       // wave's own reads of it have returned too.
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -208,7 +218,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillParams a
         // Every key of the tile exists and every block id is valid.
 #pragma unroll
         for (int i = 0; i < KI; ++i) {
-          const size_t base = (bs8 && RPI * i >= 8) ? base_hi : base_lo;
+          const size_t base = (split && RPI * i >= 8) ? base_hi : base_lo;
           lds_dma16(kpool + base, koff[i], kl + i * 1024);
           lds_dma16(vpool + base, voff[i], vl + i * 1024);
         }
@@ -216,8 +226,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillParams a
 #pragma unroll
         for (int i = 0; i < KI; ++i) {
           const int r = RPI * i + lrow;
-          const bool hi = bs8 && r >= 8;
-          const bool ok = ts + wave * 16 + r < n && phys_ok(hi ? phys_hi : phys_lo);
+          const bool hi = split && r >= 8;
+          const bool ok = ts + wave * KPW + r < n && phys_ok(hi ? phys_hi : phys_lo);
           const size_t base = hi ? base_hi : base_lo;
           lds_dma16(ok ? static_cast<const void*>(kpool + base + koff[i]) : &kZeroChunk, kl + i * 1024);
           lds_dma16(ok ? static_cast<const void*>(vpool + base + voff[i]) : &kZeroChunk, vl + i * 1024);
@@ -228,7 +238,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillParams a
       if (full) {
 #pragma unroll
         for (int i = 0; i < KI; ++i) {
-          const size_t base = (bs8 && RPI * i >= 8) ? base_hi : base_lo;
+          const size_t base = (split && RPI * i >= 8) ? base_hi : base_lo;
           kraw[i] = *reinterpret_cast<const uint2*>(kpool + base + koff[i]);
           vraw[i] = *reinterpret_cast<const uint2*>(vpool + base + voff[i]);
         }
@@ -236,8 +246,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillParams a
 #pragma unroll
         for (int i = 0; i < KI; ++i) {
           const int r = RPI * i + lrow;
-          const bool hi = bs8 && r >= 8;
-          const bool ok = ts + wave * 16 + r < n && phys_ok(hi ? phys_hi : phys_lo);
+          const bool hi = split && r >= 8;
+          const bool ok = ts + wave * KPW + r < n && phys_ok(hi ? phys_hi : phys_lo);
           const size_t base = hi ? base_hi : base_lo;
           kraw[i] = *reinterpret_cast<const uint2*>(ok ? static_cast<const void*>(kpool + base + koff[i]) : &kZeroChunk);
           vraw[i] = *reinterpret_cast<const uint2*>(ok ? static_cast<const void*>(vpool + base + voff[i]) : &kZeroChunk);
@@ -254,7 +264,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_kernel(PrefillParams a
     } else {
 #pragma unroll
       for (int i = 0; i < KI; ++i) {
-        const int row = wave * 16 + RPI * i + lrow;
+        const int row = wave * KPW + RPI * i + lrow;
         *reinterpret_cast<uint4*>(&k_s[buf][row * D + lch * 8]) = widen_e4m3x8(kraw[i]);
         *reinterpret_cast<uint4*>(&v_s[buf][row * D + lch * 8]) = widen_e4m3x8(vraw[i]);
       }
@@ -434,7 +444,7 @@ int32_t prefill_impl(void* out, const void* q, const void* k_pool, const void* v
                      int32_t total_q, int32_t max_q_len, int32_t num_q_heads,
                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                      int32_t num_blocks, float scale, float k_scale, float v_scale,
-                     int32_t sliding_window, int esz, void* stream) {
+                     int32_t sliding_window, int esz, void* stream, int waves) {
   if (head_dim != 64 && head_dim != 128 && head_dim != 256)
     return fail(PAGED_ERR_INVALID_ARG, "head_dim must be 64, 128 or 256 (got %d)", head_dim);
   if (!pow2_in(block_size, 8, 64))
@@ -454,7 +464,9 @@ int32_t prefill_impl(void* out, const void* q, const void* k_pool, const void* v
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
     return fail(PAGED_ERR_INVALID_ARG, "misaligned pointer");
   const int group = num_q_heads / num_kv_heads;
-  const int64_t tiles = (static_cast<int64_t>(max_q_len) * group + kTileM - 1) / kTileM;
+  const int nw = (waves == 4 || waves == 8) && head_dim < 256 ? waves : default_waves(head_dim);
+  const int tm = nw * kRowsPerWave;
+  const int64_t tiles = (static_cast<int64_t>(max_q_len) * group + tm - 1) / tm;
   const int64_t items = tiles * num_kv_heads * batch;
   if (items > (1LL << 30)) return fail(PAGED_ERR_INVALID_ARG, "problem too large");
   PrefillParams prm{};
@@ -479,22 +491,20 @@ int32_t prefill_impl(void* out, const void* q, const void* k_pool, const void* v
   prm.v_scale = v_scale;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid(static_cast<unsigned>(prm.per_xcd * kNumXcd));
-  const dim3 block(kWaves * 64);
+  const dim3 block(nw * 64);
   LaunchTrace tr(PAGED_KERNEL_PREFILL, s);
-  if (esz == 1) {
-    if (head_dim == 64)
-      hipExtLaunchKernelGGL(prefill_kernel<64, 1>, grid, block, 0, s, tr.start(), tr.stop(), 0, prm);
-    else if (head_dim == 128)
-      hipExtLaunchKernelGGL(prefill_kernel<128, 1>, grid, block, 0, s, tr.start(), tr.stop(), 0, prm);
-    else
-      hipExtLaunchKernelGGL(prefill_kernel<256, 1>, grid, block, 0, s, tr.start(), tr.stop(), 0, prm);
+  auto launch = [&](auto kern) {
+    hipExtLaunchKernelGGL(kern, grid, block, 0, s, tr.start(), tr.stop(), 0, prm);
+  };
+  if (head_dim == 256) {
+    if (esz == 1) launch(prefill_kernel<256, 1, 4>);
+    else launch(prefill_kernel<256, 2, 4>);
+  } else if (head_dim == 128) {
+    if (esz == 1) nw == 8 ? launch(prefill_kernel<128, 1, 8>) : launch(prefill_kernel<128, 1, 4>);
+    else nw == 8 ? launch(prefill_kernel<128, 2, 8>) : launch(prefill_kernel<128, 2, 4>);
   } else {
-    if (head_dim == 64)
-      hipExtLaunchKernelGGL(prefill_kernel<64, 2>, grid, block, 0, s, tr.start(), tr.stop(), 0, prm);
-    else if (head_dim == 128)
-      hipExtLaunchKernelGGL(prefill_kernel<128, 2>, grid, block, 0, s, tr.start(), tr.stop(), 0, prm);
-    else
-      hipExtLaunchKernelGGL(prefill_kernel<256, 2>, grid, block, 0, s, tr.start(), tr.stop(), 0, prm);
+    if (esz == 1) nw == 8 ? launch(prefill_kernel<64, 1, 8>) : launch(prefill_kernel<64, 1, 4>);
+    else nw == 8 ? launch(prefill_kernel<64, 2, 8>) : launch(prefill_kernel<64, 2, 4>);
   }
   tr.finish();
   return check_launch("paged_attn_prefill_chunk");
