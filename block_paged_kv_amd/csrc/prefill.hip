@@ -271,30 +271,32 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
     }
   };
 
-  // One K/V tile: S^T = K Q^T, online softmax, O += P V. Instantiated twice:
-  // tiles that lie wholly inside every row's [lo, a] range skip the mask.
-  auto compute_tile = [&](bool need_mask, int ts, const uint16_t* ks_buf, const uint16_t* vs_buf) {
-    // ---- S^T = K Q^T : 4 key sub-tiles x 2 query tiles ----------------------
-    // The S^T burst runs at raised wave priority: while one wave issues its
-    // back-to-back MFMAs, the other wave on the SIMD fills the gaps with its
-    // softmax work (measured: about 4% faster than equal priority).
-    __builtin_amdgcn_s_setprio(1);
-    floatx4_t s[2][4];
+  // One K/V tile in three parts: S^T = K Q^T (matrix core), the online
+  // softmax (vector ALU), O += P V (matrix core). A score array carries the
+  // first part's result to the second, pa the probabilities to the third.
+  typedef floatx4_t Scores[2][4];
+  uint4 pa[2][2];  // P as bf16 A operands: [query tile][32-key step]
+
+  // ---- S^T = K Q^T, key sub-tiles t4 in [t0, t1) x 2 query tiles --------------
+  auto tile_s = [&](Scores& sc, const uint16_t* ks_buf, int t0, int t1) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int t4 = t0; t4 < t1; ++t4) {
 #pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) s[j][t4] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4)
+      for (int j = 0; j < 2; ++j) sc[j][t4] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const uint4 ka = *reinterpret_cast<const uint4*>(&ks_buf[(t4 * 16 + lq) * D + (((4 * ks + lg) ^ swz_k(lq)) << 3)]);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) s[j][t4] = mfma16x16x32(ka, qreg[j][ks], s[j][t4]);
+        for (int j = 0; j < 2; ++j) sc[j][t4] = mfma16x16x32(ka, qreg[j][ks], sc[j][t4]);
       }
+    }
+  };
 
-    // ---- online softmax (lane: query 16j+lq, keys ts + 16*t4 + 4*lg + i) ------
-    __builtin_amdgcn_s_setprio(0);
+  // ---- online softmax (lane: query 16j+lq, keys ts + 16*t4 + 4*lg + i) --------
+  // Tiles that lie wholly inside every row's [lo, a] range skip the mask. The
+  // probabilities are produced in two halves (keys 0-31, then 32-63); `mid`
+  // runs between them.
+  auto tile_softmax = [&](Scores& sc, bool need_mask, int ts, auto&& mid) {
     if (need_mask) {
       // Rows past the tile's last row keep their (zero-query) scores: their
       // outputs are never stored. The empty asm makes the bounds opaque so
@@ -309,7 +311,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int e = t4 * 16 + i;
-            if (e < lo_rel || e > hi_rel) s[j][t4][i] = kNegInf;
+            if (e < lo_rel || e > hi_rel) sc[j][t4][i] = kNegInf;
           }
       }
     }
@@ -317,10 +319,10 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
     float mxc[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      float mx = fmaxf(s[j][0][0], s[j][0][1]);
+      float mx = fmaxf(sc[j][0][0], sc[j][0][1]);
 #pragma unroll
       for (int e = 2; e < 16; e += 2)
-        mx = fmaxf(fmaxf(mx, s[j][e >> 2][e & 3]), s[j][e >> 2][(e & 3) + 1]);
+        mx = fmaxf(fmaxf(mx, sc[j][e >> 2][e & 3]), sc[j][e >> 2][(e & 3) + 1]);
       mxc[j] = max_across_groups(mx) * c;
     }
     // Lazy rescaling: keep the reference max mc[j] until a score exceeds it by
@@ -347,29 +349,31 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
         for (int i = 0; i < 4; ++i) lsum[j][i] *= al[i];
       }
     }
-    uint4 pa[2][2];  // P as bf16 A operands: [query tile][32-key step]
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      float pr[4][4];
+    for (int kk = 0; kk < 2; ++kk) {
+      if (kk == 1) mid();
 #pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4)
+      for (int j = 0; j < 2; ++j) {
+        float pr[2][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pr[t4][i] = fast_exp2(fmaf(s[j][t4][i], c, negc[j]));
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        pa[j][kk].x = pack_bf16x2(pr[2 * kk][0], pr[2 * kk][1]);
-        pa[j][kk].y = pack_bf16x2(pr[2 * kk][2], pr[2 * kk][3]);
-        pa[j][kk].z = pack_bf16x2(pr[2 * kk + 1][0], pr[2 * kk + 1][1]);
-        pa[j][kk].w = pack_bf16x2(pr[2 * kk + 1][2], pr[2 * kk + 1][3]);
+          for (int i = 0; i < 4; ++i) pr[h][i] = fast_exp2(fmaf(sc[j][2 * kk + h][i], c, negc[j]));
+        pa[j][kk].x = pack_bf16x2(pr[0][0], pr[0][1]);
+        pa[j][kk].y = pack_bf16x2(pr[0][2], pr[0][3]);
+        pa[j][kk].z = pack_bf16x2(pr[1][0], pr[1][1]);
+        pa[j][kk].w = pack_bf16x2(pr[1][2], pr[1][3]);
       }
     }
+  };
 
-    // ---- O += P V -------------------------------------------------------------
-    // B operand of step kk for lane (lq, lg): keys 32kk + 4lg + 0..3 and
-    // 32kk + 16 + 4lg + 0..3 (the key set of this lane's P elements) at head_dim
-    // column 16nt + lq. ds_read_b64_tr_b16 gives lane j of a 16-lane group
-    // element j%4 of the rows addressed by lanes 4k + j/4 (k = 0..3): lane j
-    // addresses row key0 + j/4, columns 16nt + 4(j%4) .. +3.
+  // ---- O += P V ---------------------------------------------------------------
+  // B operand of step kk for lane (lq, lg): keys 32kk + 4lg + 0..3 and
+  // 32kk + 16 + 4lg + 0..3 (the key set of this lane's P elements) at head_dim
+  // column 16nt + lq. ds_read_b64_tr_b16 gives lane j of a 16-lane group
+  // element j%4 of the rows addressed by lanes 4k + j/4 (k = 0..3): lane j
+  // addresses row key0 + j/4, columns 16nt + 4(j%4) .. +3.
+  auto tile_pv = [&](const uint16_t* vs_buf) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
@@ -389,22 +393,33 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
     }
   };
 
+  // A tile needs the mask when it reaches past the first row's position or
+  // starts before the last row's window start.
+  auto needs_mask = [&](int ts) { return (ts + kTileN - 1 > a_min) || (ts < lo_max); };
+
   int ent_next = load_entries(kt_begin + 1);
   stage_load(kt_begin, load_entries(kt_begin), 0);
   stage_store(0);
   __syncthreads();
 
+  // Each tile through all three parts, tile kt+1 streaming into the other
+  // buffer meanwhile. The S^T burst runs at raised wave priority, so that a
+  // wave issuing back-to-back MFMAs is not held up by the softmax work of the
+  // other wave on its SIMD, which fills the gaps.
+  Scores sc;
   for (int kt = kt_begin; kt <= kt_end; ++kt) {
     const int buf = (kt - kt_begin) & 1;
     const bool has_next = kt < kt_end;
-    if (has_next) {  // tile kt+1 streams into the other buffer while tile kt computes
+    if (has_next) {
       stage_load(kt + 1, ent_next, buf ^ 1);
       ent_next = load_entries(kt + 2);
     }
     const int ts = kt * kTileN;
-    // A tile needs the mask when it reaches past the first row's position or
-    // starts before the last row's window start.
-    compute_tile((ts + kTileN - 1 > a_min) || (ts < lo_max), ts, k_s[buf], v_s[buf]);
+    __builtin_amdgcn_s_setprio(1);
+    tile_s(sc, k_s[buf], 0, 4);
+    __builtin_amdgcn_s_setprio(0);
+    tile_softmax(sc, needs_mask(ts), ts, [] {});
+    tile_pv(v_s[buf]);
     if (has_next) stage_store(buf ^ 1);
     __syncthreads();
   }
