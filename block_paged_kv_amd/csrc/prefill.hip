@@ -33,15 +33,16 @@
 namespace pagedkv {
 namespace {
 
-constexpr int kRowsPerWave = 32;
+// Query rows per wave: 32 (two 16-row MFMA tiles) up to head_dim 128, 16 at
+// head_dim 256, where two tiles' accumulators would leave one wave per SIMD.
+constexpr int rows_per_wave(int d) { return d >= 256 ? 16 : 32; }
 constexpr int kTileN = 64;                      // keys per K/V tile
-// Waves per workgroup: eight by default up to head_dim 128 (256 query rows
-// share each staged K/V tile; the workgroup fills a CU's registers), four at
-// head_dim 256, whose waves need more than 256 registers (one wave per SIMD;
-// the 128 KiB of tiles allow one workgroup), and four when decode
-// workgroups run beside the prefill (mixed step), so that a CU can hold one
-// of each.
-constexpr int default_waves(int d) { return d >= 256 ? 4 : 8; }
+// Waves per workgroup: eight by default (up to head_dim 128, 256 query rows
+// share each staged K/V tile and the workgroup fills a CU's registers; at
+// head_dim 256, 8 x 16 rows, two waves per SIMD, the 128 KiB of tiles allow
+// one workgroup), and four up to head_dim 128 when decode workgroups run
+// beside the prefill (mixed step), so that a CU can hold one of each.
+constexpr int default_waves(int) { return 8; }
 constexpr int kNumXcd = 8;
 
 typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
@@ -72,7 +73,9 @@ __device__ __forceinline__ floatx4_t mfma16x16x32(const uint4& a, const uint4& b
 template <int D, int ESZ, int NW>
 __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill_kernel(PrefillParams a) {
   constexpr int kWaves = NW;
-  constexpr int kTileM = NW * kRowsPerWave;
+  constexpr int RPW = rows_per_wave(D);
+  constexpr int JT = RPW / 16;  // 16-row query tiles per wave
+  constexpr int kTileM = NW * RPW;
   // LDS tiles: key rows of D bf16 elements, unpadded; the 16-byte chunks of
   // a row are stored XOR-swizzled (chunk c of row r at position c ^ swz(r))
   // so that both read patterns below are free of bank conflicts: K reads 16
@@ -122,12 +125,12 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
   const int lg = lane >> 4;   // lane group 0..3
 
   // Query rows of this lane in the S^T layout: wave rows 16j + lq.
-  int qpos[2], qlo[2];
-  bool qvalid[2];
-  uint4 qreg[2][KS];
+  int qpos[JT], qlo[JT];
+  bool qvalid[JT];
+  uint4 qreg[JT][KS];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int r = r_first + wave * kRowsPerWave + 16 * j + lq;
+  for (int j = 0; j < JT; ++j) {
+    const int r = r_first + wave * RPW + 16 * j + lq;
     qvalid[j] = r <= r_last;
     const int pos = qvalid[j] ? r / G : 0;
     const int g = qvalid[j] ? r - pos * G : 0;
@@ -140,18 +143,23 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
                               : make_uint4(0, 0, 0, 0);
   }
 
-  floatx4_t o[2][NT];
+  floatx4_t o[JT][NT];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < JT; ++j)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) o[j][nt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   // Reference max per query row in scaled log2 units (scale > 0, so the max
   // of the raw scores scales to it), and its negation for the exponent.
-  float mc[2] = {kNegInf, kNegInf};
-  float negc[2] = {0.f, 0.f};
+  float mc[JT], negc[JT];
   // Row sums accumulate on the matrix core: P times a ones tile gives, in the
   // O layout, the sum of the same bf16 probabilities the numerator uses.
-  floatx4_t lsum[2] = {floatx4_t{0.f, 0.f, 0.f, 0.f}, floatx4_t{0.f, 0.f, 0.f, 0.f}};
+  floatx4_t lsum[JT];
+#pragma unroll
+  for (int j = 0; j < JT; ++j) {
+    mc[j] = kNegInf;
+    negc[j] = 0.f;
+    lsum[j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  }
   const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
 
   const int32_t* bt = a.bt + static_cast<size_t>(b) * a.mb;
@@ -274,20 +282,20 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
   // One K/V tile in three parts: S^T = K Q^T (matrix core), the online
   // softmax (vector ALU), O += P V (matrix core). A score array carries the
   // first part's result to the second, pa the probabilities to the third.
-  typedef floatx4_t Scores[2][4];
-  uint4 pa[2][2];  // P as bf16 A operands: [query tile][32-key step]
+  typedef floatx4_t Scores[JT][4];
+  uint4 pa[JT][2];  // P as bf16 A operands: [query tile][32-key step]
 
   // ---- S^T = K Q^T, key sub-tiles t4 in [t0, t1) x 2 query tiles --------------
   auto tile_s = [&](Scores& sc, const uint16_t* ks_buf, int t0, int t1) {
 #pragma unroll
     for (int t4 = t0; t4 < t1; ++t4) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) sc[j][t4] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < JT; ++j) sc[j][t4] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const uint4 ka = *reinterpret_cast<const uint4*>(&ks_buf[(t4 * 16 + lq) * D + (((4 * ks + lg) ^ swz_k(lq)) << 3)]);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) sc[j][t4] = mfma16x16x32(ka, qreg[j][ks], sc[j][t4]);
+        for (int j = 0; j < JT; ++j) sc[j][t4] = mfma16x16x32(ka, qreg[j][ks], sc[j][t4]);
       }
     }
   };
@@ -302,7 +310,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
       // outputs are never stored. The empty asm makes the bounds opaque so
       // the compares stay inside this rarely taken branch.
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < JT; ++j) {
         int lo_rel = qlo[j] - ts - 4 * lg;
         int hi_rel = qpos[j] - ts - 4 * lg;
         asm volatile("" : "+v"(lo_rel), "+v"(hi_rel));
@@ -316,9 +324,9 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
       }
     }
     // Row maxima in scaled log2 units; chained pairs so each step is one v_max3_f32.
-    float mxc[2];
+    float mxc[JT];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < JT; ++j) {
       float mx = fmaxf(sc[j][0][0], sc[j][0][1]);
 #pragma unroll
       for (int e = 2; e < 16; e += 2)
@@ -328,11 +336,14 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
     // Lazy rescaling: keep the reference max mc[j] until a score exceeds it by
     // more than 2^8 (in log2 units); until then probabilities stay <= 256,
     // harmless in fp32 and bf16, and the final division by the sum taken with
-    // the same reference cancels the choice exactly. One vote covers both
-    // query tiles, so the common path has no branch between the two.
-    if (__any(mxc[0] > mc[0] + 8.f || mxc[1] > mc[1] + 8.f)) {
+    // the same reference cancels the choice exactly. One vote covers the
+    // wave's query tiles, so the common path has no branch between them.
+    bool up = false;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < JT; ++j) up = up || mxc[j] > mc[j] + 8.f;
+    if (__any(up)) {
+#pragma unroll
+      for (int j = 0; j < JT; ++j) {
         const float mnew = fmaxf(mc[j], mxc[j]);
         const float alpha = mnew == kNegInf ? 1.f : fast_exp2(mc[j] - mnew);
         mc[j] = mnew;
@@ -353,7 +364,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
     for (int kk = 0; kk < 2; ++kk) {
       if (kk == 1) mid();
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < JT; ++j) {
         float pr[2][4];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
@@ -377,7 +388,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) lsum[j] = mfma16x16x32(pa[j][kk], ones, lsum[j]);
+      for (int j = 0; j < JT; ++j) lsum[j] = mfma16x16x32(pa[j][kk], ones, lsum[j]);
       const int vrow = kk * 32 + 4 * lg + (lq >> 2);  // and vrow + 16: same swizzle
       const uint16_t* vbase = &vs_buf[vrow * D + 4 * (lq & 1)];
       const int vsw = swz_v(vrow);
@@ -388,7 +399,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
         const uint2 v1 = ds_read_tr16(vbase + 16 * D + vc);
         const uint4 vb = make_uint4(v0.x, v0.y, v1.x, v1.y);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) o[j][nt] = mfma16x16x32(pa[j][kk], vb, o[j][nt]);
+        for (int j = 0; j < JT; ++j) o[j][nt] = mfma16x16x32(pa[j][kk], vb, o[j][nt]);
       }
     }
   };
@@ -426,13 +437,13 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
 
   // ---- normalise and store --------------------------------------------------
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < JT; ++j) {
     float inv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) inv[i] = lsum[j][i] > 0.f ? a.v_scale / lsum[j][i] : 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = r_first + wave * kRowsPerWave + 16 * j + 4 * lg + i;
+      const int r = r_first + wave * RPW + 16 * j + 4 * lg + i;
       if (r > r_last) continue;
       const int pos = r / G;
       const int g = r - pos * G;
@@ -480,7 +491,7 @@ int32_t prefill_impl(void* out, const void* q, const void* k_pool, const void* v
     return fail(PAGED_ERR_INVALID_ARG, "misaligned pointer");
   const int group = num_q_heads / num_kv_heads;
   const int nw = (waves == 4 || waves == 8) && head_dim < 256 ? waves : default_waves(head_dim);
-  const int tm = nw * kRowsPerWave;
+  const int tm = nw * rows_per_wave(head_dim);
   const int64_t tiles = (static_cast<int64_t>(max_q_len) * group + tm - 1) / tm;
   const int64_t items = tiles * num_kv_heads * batch;
   if (items > (1LL << 30)) return fail(PAGED_ERR_INVALID_ARG, "problem too large");
@@ -512,8 +523,8 @@ int32_t prefill_impl(void* out, const void* q, const void* k_pool, const void* v
     hipExtLaunchKernelGGL(kern, grid, block, 0, s, tr.start(), tr.stop(), 0, prm);
   };
   if (head_dim == 256) {
-    if (esz == 1) launch(prefill_kernel<256, 1, 4>);
-    else launch(prefill_kernel<256, 2, 4>);
+    if (esz == 1) launch(prefill_kernel<256, 1, 8>);
+    else launch(prefill_kernel<256, 2, 8>);
   } else if (head_dim == 128) {
     if (esz == 1) nw == 8 ? launch(prefill_kernel<128, 1, 8>) : launch(prefill_kernel<128, 1, 4>);
     else nw == 8 ? launch(prefill_kernel<128, 2, 8>) : launch(prefill_kernel<128, 2, 4>);
