@@ -384,9 +384,13 @@ struct StageGeo {
   static constexpr int NSLOT = D >= 512 ? 1 : 2;
   static constexpr int STAGE = 2 * SBYTES;                 // K then V rows of one stage
   static constexpr int WIDE = ESZ == 1 ? 16 * VROWB : 0;   // FP8: the widened V rows
-  // Ring slot 0 doubles as the wave-merge buffer (16 heads x D floats); with
-  // one slot it also holds the widened V rows after the stage.
-  static constexpr int MERGE = 16 * D * 4;
+  // Ring slot 0 doubles as the wave-merge buffer (MERGE_ROWS heads x D
+  // floats per pass; groups of more heads merge in two passes); with one
+  // slot it also holds the widened V rows after the stage. FP8 stages are
+  // half the size of bf16 ones, so their merge takes 8 heads per pass and a
+  // workgroup's rings stay within 48 KiB at head_dim 128 (three per CU).
+  static constexpr int MERGE_ROWS = (ESZ == 1 && D <= 256) ? 8 : 16;
+  static constexpr int MERGE = MERGE_ROWS * D * 4;
   static constexpr int SLOT0_DATA = NSLOT == 1 ? STAGE + WIDE : STAGE;
   static constexpr int SLOT0 = SLOT0_DATA > MERGE ? SLOT0_DATA : MERGE;
   // Slot 1 (two slots) or, with one slot, just the merge's (max, sum) rows.
@@ -579,17 +583,34 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_lds_kernel(D
     // layout as the bf16 kernel reads). Only this wave touches the tile, and a
     // wave's LDS accesses are performed in order.
     const char* vr_bf = vr_in;
+    auto k_code_chunk = [&](int ks) { return (2 * ks + (lg >> 1)) ^ (lq & SWZ); };
+    uint2 kraw[KV8 && KB == KS ? KS : 1];
     if constexpr (KV8) {
       char* vw = WIDE_ARRAY ? reinterpret_cast<char*>(&vwide[wave][0])
                             : reinterpret_cast<char*>(&ring0[wave][0]) + Sg::STAGE;
+      // The stage's K codes (this lane's fragments) and V codes are requested
+      // together, ahead of the V tile's widening stores, so one LDS round
+      // trip serves both.
+      if constexpr (KB == KS) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          kraw[ks] = *reinterpret_cast<const uint2*>(kr + lq * ROWB + k_code_chunk(ks) * 16 + 8 * (lg & 1));
+      }
+      uint4 c8[CPT / 4];
 #pragma unroll
       for (int j = 0; j < CPT / 4; ++j) {
         const int q = lane + 64 * j;  // fp8 chunk: row q / CPT, 16 elements (q % CPT)*16 ..
         const int row = q / CPT;
         const int cc = q % CPT;
-        const uint4 c8 = *reinterpret_cast<const uint4*>(vr_in + row * ROWB + ((cc ^ (row & SWZ)) << 4));
-        const uint4 lo = widen_e4m3x8(make_uint2(c8.x, c8.y));
-        const uint4 hi = widen_e4m3x8(make_uint2(c8.z, c8.w));
+        c8[j] = *reinterpret_cast<const uint4*>(vr_in + row * ROWB + ((cc ^ (row & SWZ)) << 4));
+      }
+#pragma unroll
+      for (int j = 0; j < CPT / 4; ++j) {
+        const int q = lane + 64 * j;
+        const int row = q / CPT;
+        const int cc = q % CPT;
+        const uint4 lo = widen_e4m3x8(make_uint2(c8[j].x, c8[j].y));
+        const uint4 hi = widen_e4m3x8(make_uint2(c8[j].z, c8[j].w));
         *reinterpret_cast<uint4*>(vw + row * VROWB + (((2 * cc) ^ (row & VSWZ)) << 4)) = lo;
         *reinterpret_cast<uint4*>(vw + row * VROWB + (((2 * cc + 1) ^ (row & VSWZ)) << 4)) = hi;
       }
@@ -602,8 +623,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_lds_kernel(D
     // returns keys 4*lg .. 4*lg+3 of column 16*nt + lq.
     auto read_k = [&](int ks) -> uint4 {
       if constexpr (KV8) {
-        const int chunk = (2 * ks + (lg >> 1)) ^ (lq & SWZ);
-        return widen_e4m3x8(*reinterpret_cast<const uint2*>(kr + lq * ROWB + chunk * 16 + 8 * (lg & 1)));
+        if constexpr (KB == KS) return widen_e4m3x8(kraw[ks]);
+        return widen_e4m3x8(*reinterpret_cast<const uint2*>(kr + lq * ROWB + k_code_chunk(ks) * 16 + 8 * (lg & 1)));
       } else {
         const int chunk = (4 * ks + lg) ^ (lq & SWZ);
         return *reinterpret_cast<const uint4*>(kr + lq * ROWB + chunk * 16);
@@ -734,63 +755,71 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_lds_kernel(D
 
   // ---- merge the waves and store -------------------------------------------
   // Each wave puts its (max, sum) and accumulator rows in its own ring slots
-  // (only it has used them), so one barrier suffices before the merge.
-  {
-    float* my_o = reinterpret_cast<float*>(&ring0[wave][0]);   // [16][D]
-    float* my_ml = reinterpret_cast<float*>(&ring1[wave][0]);  // [16][2]
-    static_assert(Sg::SLOT0 >= 16 * D * static_cast<int>(sizeof(float)), "merge buffer does not fit");
-    // Lanes holding any of the GT real rows write all four of theirs (rows
-    // up to 15 stay inside the slot).
-    if (4 * lg < GT) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) my_o[(4 * lg + i) * D + 16 * nt + lq] = o[nt][i];
-      if (lq == 0)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) my_ml[(4 * lg + i) * 2 + 1] = lsum[i];
-    }
-    if (lg == 0 && lq < GT) my_ml[lq * 2] = mc;
-  }
-  __syncthreads();
+  // (only it has used them), so one barrier suffices before a merge pass; a
+  // pass covers MERGE_ROWS query heads.
+  constexpr int MR = Sg::MERGE_ROWS;
+  static_assert(Sg::SLOT0 >= MR * D * static_cast<int>(sizeof(float)), "merge buffer does not fit");
+  static_assert(Sg::SLOT1 >= MR * 2 * static_cast<int>(sizeof(float)), "merge buffer does not fit");
   const float* sm_o = reinterpret_cast<const float*>(ring0);
   const float* sm_ml = reinterpret_cast<const float*>(ring1);
   constexpr int kO = Sg::SLOT0 / 4;      // floats between two waves' accumulator rows
   constexpr int kML = Sg::SLOT1 / 4;     // floats between two waves' (max, sum) rows
-  for (int idx = threadIdx.x; idx < GT * D; idx += blockDim.x) {
-    const int g = idx / D;
-    const int d = idx - g * D;
-    // Every wave slot is read at once (all lie inside the rings); the entries
-    // of waves past nw, which did not run, are then ignored.
-    float mw[kDecodeWaves], lw[kDecodeWaves], ow[kDecodeWaves];
+  for (int g0 = 0; g0 < GT; g0 += MR) {
+    if (g0 > 0) __syncthreads();  // the previous pass has read the buffers
+    const int g1 = min(GT, g0 + MR);
+    {
+      float* my_o = reinterpret_cast<float*>(&ring0[wave][0]);   // [MR][D]
+      float* my_ml = reinterpret_cast<float*>(&ring1[wave][0]);  // [MR][2]
+      // Lanes holding any of the pass's real rows write all four of theirs
+      // (rows up to g0 + MR - 1 stay inside the slot).
+      if (4 * lg >= g0 && 4 * lg < g1) {
 #pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) {
-      const float2 ml = *reinterpret_cast<const float2*>(sm_ml + w * kML + g * 2);
-      mw[w] = ml.x;
-      lw[w] = ml.y;
-      ow[w] = sm_o[w * kO + g * D + d];
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) my_o[(4 * lg - g0 + i) * D + 16 * nt + lq] = o[nt][i];
+        if (lq == 0)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) my_ml[(4 * lg - g0 + i) * 2 + 1] = lsum[i];
+      }
+      if (lg == 0 && lq >= g0 && lq < g1) my_ml[(lq - g0) * 2] = mc;
     }
-    float M = kNegInf;
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < (g1 - g0) * D; idx += blockDim.x) {
+      const int gl = idx / D;
+      const int g = g0 + gl;
+      const int d = idx - gl * D;
+      // Every wave slot is read at once (all lie inside the rings); the entries
+      // of waves past nw, which did not run, are then ignored.
+      float mw[kDecodeWaves], lw[kDecodeWaves], ow[kDecodeWaves];
 #pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) M = w < nw ? fmaxf(M, mw[w]) : M;
-    float L = 0.f, A = 0.f;
+      for (int w = 0; w < kDecodeWaves; ++w) {
+        const float2 ml = *reinterpret_cast<const float2*>(sm_ml + w * kML + gl * 2);
+        mw[w] = ml.x;
+        lw[w] = ml.y;
+        ow[w] = sm_o[w * kO + gl * D + d];
+      }
+      float M = kNegInf;
 #pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) {
-      const bool live = w < nw && mw[w] != kNegInf;
-      const float f = live ? fast_exp2(mw[w] - M) : 0.f;
-      L = live ? fmaf(lw[w], f, L) : L;
-      A = live ? fmaf(ow[w], f, A) : A;
-    }
-    const size_t bh = static_cast<size_t>(b) * a.hq + h0 + g;
-    A *= a.v_scale;  // FP8: V codes stand for v_scale * value (1 for bf16: exact)
-    if (a.out) {
-      store_out<2>(a.out, bh * D + d, L > 0.f ? A / L : 0.f);
-    } else {
-      const size_t slot = bh * a.max_parts + p;
-      a.ws_acc[slot * D + d] = A;
-      if (d == 0) {
-        a.ws_ml[slot * 2] = M;
-        a.ws_ml[slot * 2 + 1] = L;
+      for (int w = 0; w < kDecodeWaves; ++w) M = w < nw ? fmaxf(M, mw[w]) : M;
+      float L = 0.f, A = 0.f;
+#pragma unroll
+      for (int w = 0; w < kDecodeWaves; ++w) {
+        const bool live = w < nw && mw[w] != kNegInf;
+        const float f = live ? fast_exp2(mw[w] - M) : 0.f;
+        L = live ? fmaf(lw[w], f, L) : L;
+        A = live ? fmaf(ow[w], f, A) : A;
+      }
+      const size_t bh = static_cast<size_t>(b) * a.hq + h0 + g;
+      A *= a.v_scale;  // FP8: V codes stand for v_scale * value (1 for bf16: exact)
+      if (a.out) {
+        store_out<2>(a.out, bh * D + d, L > 0.f ? A / L : 0.f);
+      } else {
+        const size_t slot = bh * a.max_parts + p;
+        a.ws_acc[slot * D + d] = A;
+        if (d == 0) {
+          a.ws_ml[slot * 2] = M;
+          a.ws_ml[slot * 2 + 1] = L;
+        }
       }
     }
   }
@@ -955,12 +984,13 @@ int32_t make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, int3
     // another's streaming; eight waves in one workgroup measured slower).
     const int32_t unit = std::max(kStageTokens, block_size);
     if (part == 0) {
-      // Aim at every wave slot of the device busy at once (8 waves per CU, 4
-      // at head_dim 256 and 512 where a workgroup's rings take most of the LDS) with
+      // Aim at every wave slot of the device busy at once (8 waves per CU; 12
+      // over FP8 pools up to head_dim 128, whose rings are smaller; 4 at
+      // head_dim 256 and 512 where a workgroup's rings take most of the LDS) with
       // whole stages per wave; longer rows get longer partitions.
       const int cus = device_cu_count();
       if (cus <= 0) return fail(PAGED_ERR_HIP, "cannot query the device compute-unit count");
-      const int64_t slots = static_cast<int64_t>(head_dim >= 256 ? 4 : 8) * cus;
+      const int64_t slots = static_cast<int64_t>(head_dim >= 256 ? 4 : (esz == 1 && head_dim <= 128) ? 12 : 8) * cus;
       const int64_t stages = pairs * ((span + kStageTokens - 1) / kStageTokens);
       int64_t spw = std::max<int64_t>(1, (stages + slots - 1) / slots);
       int64_t p2 = 1;
