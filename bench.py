@@ -280,6 +280,9 @@ def main():
     ap.add_argument("--waves", type=int, default=None, help="independent batches rotated through")
     ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"], help="KV pool element type")
     ap.add_argument("--head-dim", type=int, default=None, help="head_dim override (e.g. 512 for the hybrid decode)")
+    ap.add_argument("--scrub", action="store_true",
+                    help="read a 1 GiB buffer before every attention launch of the per-kernel timing pass, "
+                         "so the roofline is taken with cold caches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
@@ -426,13 +429,24 @@ def main():
     # Timed region 2 (per-kernel durations): the same steps launched eagerly,
     # the library recording a HIP event pair around every launch on the launch
     # stream (events inside a captured graph cannot be timed).
-    log(f"[bench] per-kernel timing over {steps} eager steps")
+    log(f"[bench] per-kernel timing over {steps} eager steps{' (caches scrubbed)' if args.scrub else ''}")
+    if args.scrub:
+        # A read leaves the caches holding clean, unrelated lines (a write
+        # would leave dirty ones whose write-back the next kernel would pay).
+        scrub_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        sink = torch.zeros((), dtype=torch.float32, device="cuda")
+    n_writes = sum(1 for L in wl.layers if not L.alias_of)
     pk.trace_reset()
     torch.cuda.synchronize()
     pk.trace_enable(True)
     with torch.cuda.stream(stream):
         for i in range(steps):
-            step(args.warmup + i)
+            for j, c in enumerate(calls[(args.warmup + i) % R]):
+                if args.scrub and j >= n_writes:
+                    pk.trace_enable(False)
+                    sink.copy_(scrub_buf.sum())
+                    pk.trace_enable(True)
+                c()
     torch.cuda.synchronize()
     pk.trace_enable(False)
 
@@ -532,6 +546,7 @@ def main():
         },
         "kernels": kernels,
         "timing": timing,
+        "kernel_timing_caches": "scrubbed (1 GiB read before each attention launch)" if args.scrub else "warm",
     }
     result.update(extra)
     if mixed_step:
