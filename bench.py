@@ -141,6 +141,14 @@ def counter_traffic(kern, workload):
         return None
 
 
+def launch_percentiles(pk, kern):
+    """p10 / p50 / p90 of the kernel's per-launch durations (us) in the timed pass."""
+    dur = pk.trace_durations(kern)
+    if len(dur) == 0:
+        return None
+    return [round(float(x) * 1e3, 3) for x in np.percentile(np.asarray(dur), [10, 50, 90])]
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -541,6 +549,7 @@ def main():
             "frac": round(achieved / peak, 4),
             "traffic": counter_traffic(kern, args.workload + ("_fp8" if fp8 else "")),
             "avg_launch_us": round(k_ms * 1e3 / max(k_n, 1), 3),
+            "launch_us_p10_p50_p90": launch_percentiles(pk, kern),
             "launches": k_n,
             "work_per_step": work,
         },
