@@ -52,8 +52,8 @@ extern "C" int32_t paged_attn_mixed(void* out, const void* q, const void* k_pool
   // Both parts: check what either could reject before enqueuing anything.
   if (!out || !q || !k_pool || !v_pool || !block_tables || !cu_q_lens || !seq_lens)
     return fail(PAGED_ERR_INVALID_ARG, "NULL pointer");
-  if (head_dim != 64 && head_dim != 128 && head_dim != 256)
-    return fail(PAGED_ERR_INVALID_ARG, "prefill rows need head_dim 64, 128 or 256 (got %d)", head_dim);
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256 && head_dim != 512)
+    return fail(PAGED_ERR_INVALID_ARG, "head_dim must be 64, 128, 256 or 512 (got %d)", head_dim);
   if (!std::isfinite(scale) || scale < 0.f)
     return fail(PAGED_ERR_INVALID_ARG, "scale must be finite and non-negative");
   if (!(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))

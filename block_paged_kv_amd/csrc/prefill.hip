@@ -33,16 +33,21 @@
 namespace pagedkv {
 namespace {
 
-// Query rows per wave: 32 (two 16-row MFMA tiles) up to head_dim 128, 16 at
+// Query rows per wave: 32 (two 16-row MFMA tiles) up to head_dim 128, 16 from
 // head_dim 256, where two tiles' accumulators would leave one wave per SIMD.
 constexpr int rows_per_wave(int d) { return d >= 256 ? 16 : 32; }
-constexpr int kTileN = 64;                      // keys per K/V tile
+// Keys per K/V tile: 64, except 32 at head_dim 512, where two buffers of 64
+// one-KiB key rows (K and V) would not fit in a CU's 160 KiB of LDS.
+constexpr int tile_keys(int d) { return d >= 512 ? 32 : 64; }
 // Waves per workgroup: eight by default (up to head_dim 128, 256 query rows
 // share each staged K/V tile and the workgroup fills a CU's registers; at
 // head_dim 256, 8 x 16 rows, two waves per SIMD, the 128 KiB of tiles allow
-// one workgroup), and four up to head_dim 128 when decode workgroups run
-// beside the prefill (mixed step), so that a CU can hold one of each.
-constexpr int default_waves(int) { return 8; }
+// one workgroup), four at head_dim 512 (one wave per SIMD: the accumulators
+// of 16 rows x 512 columns and the query operands need more registers than
+// two waves per SIMD leave), and four up to head_dim 128 when decode
+// workgroups run beside the prefill (mixed step), so that a CU can hold one
+// of each.
+constexpr int default_waves(int d) { return d >= 512 ? 4 : 8; }
 constexpr int kNumXcd = 8;
 
 typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
@@ -76,6 +81,9 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
   constexpr int RPW = rows_per_wave(D);
   constexpr int JT = RPW / 16;  // 16-row query tiles per wave
   constexpr int kTileM = NW * RPW;
+  constexpr int kTileN = tile_keys(D);
+  constexpr int NS = kTileN / 16;    // 16-key sub-tiles per tile (S^T column tiles)
+  constexpr int NK = kTileN / 32;    // 32-key MFMA steps of P.V per tile
   // LDS tiles: key rows of D bf16 elements, unpadded; the 16-byte chunks of
   // a row are stored XOR-swizzled (chunk c of row r at position c ^ swz(r))
   // so that both read patterns below are free of bank conflicts: K reads 16
@@ -167,7 +175,8 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
   const int bs_mask = (1 << bs_log2) - 1;
   const int kt_begin = lo_min / kTileN;
   const int kt_end = a_max / kTileN;  // inclusive
-  const int tile_blocks = kTileN >> bs_log2;  // blocks per K/V tile (block_size <= 64)
+  // Blocks a K/V tile touches: a 32-key tile lies inside one 64-key block.
+  const int tile_blocks = max(1, kTileN >> bs_log2);
   const float c = a.scale_log2;
 
   // Block-table entries of one tile, one per lane (lane < tile_blocks).
@@ -177,18 +186,18 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
   };
   auto phys_ok = [&](int phys) { return phys > 0 && phys < a.nb; };
 
-  // Staging (double buffered): wave w moves keys 16w .. 16w+15 of a tile, K
-  // and V alike. bf16 pools go straight to LDS (global_load_lds_dwordx4: one
+  // Staging (double buffered): wave w moves keys KPW*w .. KPW*w + KPW-1 of a
+  // tile, K and V alike. bf16 pools go straight to LDS (global_load_lds_dwordx4: one
   // instruction fills 1 KiB, i.e. RPI consecutive key rows; each lane names
   // the global chunk that belongs at its swizzled LDS position), so no
   // registers hold the next tile. FP8 pools are read into registers, widened
   // to bf16 and stored at the same swizzled positions.
-  // The wave's 16 keys lie in one block (block_size >= 16) or in two
-  // (block_size 8, keys 8..15 in the second): block ids come from the tile's
+  // The wave's keys lie in one block, or in two when 16 keys meet block_size
+  // 8 (keys 8..15 in the second): block ids come from the tile's
   // entries by readlane, so block bases are wave-uniform and each lane adds a
   // loop-invariant 32-bit offset.
   constexpr int RPI = 64 / DCH;                   // key rows per load instruction
-  constexpr int KPW = kTileN / kWaves;            // keys each wave stages (16 or 8)
+  constexpr int KPW = kTileN / kWaves;            // keys each wave stages (16, 8 or 4)
   constexpr int KI = KPW / RPI;                   // load instructions per wave per tile (K, and V)
   const bool bs8 = bs_log2 == 3;
   const bool split = bs8 && KPW > 8;              // the wave's keys span two blocks
@@ -282,8 +291,8 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
   // One K/V tile in three parts: S^T = K Q^T (matrix core), the online
   // softmax (vector ALU), O += P V (matrix core). A score array carries the
   // first part's result to the second, pa the probabilities to the third.
-  typedef floatx4_t Scores[JT][4];
-  uint4 pa[JT][2];  // P as bf16 A operands: [query tile][32-key step]
+  typedef floatx4_t Scores[JT][NS];
+  uint4 pa[JT][NK];  // P as bf16 A operands: [query tile][32-key step]
 
   // ---- S^T = K Q^T, key sub-tiles t4 in [t0, t1) x 2 query tiles --------------
   auto tile_s = [&](Scores& sc, const uint16_t* ks_buf, int t0, int t1) {
@@ -302,8 +311,8 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
 
   // ---- online softmax (lane: query 16j+lq, keys ts + 16*t4 + 4*lg + i) --------
   // Tiles that lie wholly inside every row's [lo, a] range skip the mask. The
-  // probabilities are produced in two halves (keys 0-31, then 32-63); `mid`
-  // runs between them.
+  // probabilities are produced in 32-key steps (keys 0-31, then 32-63 of a
+  // 64-key tile); `mid` runs between the two.
   auto tile_softmax = [&](Scores& sc, bool need_mask, int ts, auto&& mid) {
     if (need_mask) {
       // Rows past the tile's last row keep their (zero-query) scores: their
@@ -315,7 +324,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
         int hi_rel = qpos[j] - ts - 4 * lg;
         asm volatile("" : "+v"(lo_rel), "+v"(hi_rel));
 #pragma unroll
-        for (int t4 = 0; t4 < 4; ++t4)
+        for (int t4 = 0; t4 < NS; ++t4)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int e = t4 * 16 + i;
@@ -329,7 +338,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
     for (int j = 0; j < JT; ++j) {
       float mx = fmaxf(sc[j][0][0], sc[j][0][1]);
 #pragma unroll
-      for (int e = 2; e < 16; e += 2)
+      for (int e = 2; e < 4 * NS; e += 2)
         mx = fmaxf(fmaxf(mx, sc[j][e >> 2][e & 3]), sc[j][e >> 2][(e & 3) + 1]);
       mxc[j] = max_across_groups(mx) * c;
     }
@@ -355,13 +364,27 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) o[j][nt][i] *= al[i];
+          for (int i = 0; i < 4; ++i) {
+            if constexpr (D >= 512) {
+              // The accumulators live in AGPRs (the matrix core's accumulation
+              // registers) at this size; scaling them in place here keeps the
+              // compiler from carrying them through the loop in ordinary
+              // registers and copying all of them across every tile.
+              float x = o[j][nt][i];
+              float t;
+              asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                           : "+a"(x), "=&v"(t) : "v"(al[i]));
+              o[j][nt][i] = x;
+            } else {
+              o[j][nt][i] *= al[i];
+            }
+          }
 #pragma unroll
         for (int i = 0; i < 4; ++i) lsum[j][i] *= al[i];
       }
     }
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < NK; ++kk) {
       if (kk == 1) mid();
 #pragma unroll
       for (int j = 0; j < JT; ++j) {
@@ -386,7 +409,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
   // addresses row key0 + j/4, columns 16nt + 4(j%4) .. +3.
   auto tile_pv = [&](const uint16_t* vs_buf) {
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < NK; ++kk) {
 #pragma unroll
       for (int j = 0; j < JT; ++j) lsum[j] = mfma16x16x32(pa[j][kk], ones, lsum[j]);
       const int vrow = kk * 32 + 4 * lg + (lq >> 2);  // and vrow + 16: same swizzle
@@ -427,7 +450,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
     }
     const int ts = kt * kTileN;
     __builtin_amdgcn_s_setprio(1);
-    tile_s(sc, k_s[buf], 0, 4);
+    tile_s(sc, k_s[buf], 0, NS);
     __builtin_amdgcn_s_setprio(0);
     tile_softmax(sc, needs_mask(ts), ts, [] {});
     tile_pv(v_s[buf]);
@@ -471,8 +494,8 @@ int32_t prefill_impl(void* out, const void* q, const void* k_pool, const void* v
                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                      int32_t num_blocks, float scale, float k_scale, float v_scale,
                      int32_t sliding_window, int esz, void* stream, int waves) {
-  if (head_dim != 64 && head_dim != 128 && head_dim != 256)
-    return fail(PAGED_ERR_INVALID_ARG, "head_dim must be 64, 128 or 256 (got %d)", head_dim);
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256 && head_dim != 512)
+    return fail(PAGED_ERR_INVALID_ARG, "head_dim must be 64, 128, 256 or 512 (got %d)", head_dim);
   if (!pow2_in(block_size, 8, 64))
     return fail(PAGED_ERR_INVALID_ARG, "block_size must be a power of two in [8, 64]");
   if (num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads)
@@ -522,7 +545,10 @@ int32_t prefill_impl(void* out, const void* q, const void* k_pool, const void* v
   auto launch = [&](auto kern) {
     hipExtLaunchKernelGGL(kern, grid, block, 0, s, tr.start(), tr.stop(), 0, prm);
   };
-  if (head_dim == 256) {
+  if (head_dim == 512) {
+    if (esz == 1) launch(prefill_kernel<512, 1, 4>);
+    else launch(prefill_kernel<512, 2, 4>);
+  } else if (head_dim == 256) {
     if (esz == 1) launch(prefill_kernel<256, 1, 8>);
     else launch(prefill_kernel<256, 2, 8>);
   } else if (head_dim == 128) {

@@ -40,8 +40,8 @@
  *     Block 0 is the null sentinel and is never read.
  *   - A slot is physical_block * block_size + offset (int64); slot < 0 means
  *     padding.
- *   - head_dim in {64, 128, 256} (also 512 for the KV write, the gather and
- *     decode over bf16 or FP8 pools); block_size a power of two in [8, 64];
+ *   - head_dim in {64, 128, 256, 512} (512: bf16 or FP8 pools, not float32);
+ *     block_size a power of two in [8, 64];
  *     num_q_heads a multiple of num_kv_heads (query head h reads KV head
  *     h / (num_q_heads / num_kv_heads)).
  *   - The allocator is host-only C++, not thread-safe (one allocator per pool,
@@ -264,7 +264,6 @@ int32_t paged_attn_prefill_chunk_fp8(void* out, const void* q, const void* k_poo
  *   partition_tokens, max_seq_len, workspace: as for paged_attn_decode with
  *                    batch = num_decode_rows (size the workspace with
  *                    paged_attn_decode_workspace_bytes(num_decode_rows, ...))
- *   head_dim       : 64, 128 or 256 when any chunk row is present
  * Errors: those of both entry points, checked before anything is enqueued. */
 int32_t paged_attn_mixed(void* out, const void* q, const void* k_pool, const void* v_pool,
                          const int32_t* block_tables, int32_t max_blocks_per_seq,

@@ -128,20 +128,32 @@ def _suffix_tokens(b, length):
 
 def make(name, *, batch=None, hq=None, hkv=None, head_dim=None, context=None, prefix=None,
          num_blocks=None, seed=None, chunk=None, window=None, dtype=None, part=None,
-         num_prefixes=None, sliding_blocks=None, waves=None, block_size=None, kv_dtype=None):
+         num_prefixes=None, sliding_blocks=None, waves=None, block_size=None, kv_dtype=None,
+         k_growth=None):
     """Build workload ``name`` at its published sizes; keyword overrides shrink it for tests.
 
     ``block_size`` (a power of two in [8, 64], default 16) changes only the paging:
     the random draws are the same, prefix lengths round to whole blocks.
     ``kv_dtype="fp8"`` (bf16 workloads) stores the pools as FP8 E4M3 codes with a
     K and a V scale per layer: max |x| of the layer's K (V) over 448, so nothing
-    saturates; the draws are the same."""
+    saturates; the draws are the same.
+    ``k_growth=g`` multiplies the key of position t by 2^min(t // g, 12) (exact in
+    bf16 and float32): the largest score of a row then jumps every g positions, so an
+    online softmax has to rescale accumulators that already hold data."""
     bs = BLOCK_SIZE if block_size is None else int(block_size)
     seed = SEEDS[name] if seed is None else seed
     rng = np.random.default_rng(seed)
     wl = _make(name, rng, bs, batch=batch, hq=hq, hkv=hkv, head_dim=head_dim, context=context,
                prefix=prefix, num_blocks=num_blocks, chunk=chunk, window=window, dtype=dtype,
                part=part, num_prefixes=num_prefixes, sliding_blocks=sliding_blocks, waves=waves)
+    if k_growth:
+        for L in wl.layers:
+            if L.alias_of:
+                continue
+            for b, x in enumerate(L.k):
+                t = L.live_from[b] + np.arange(x.shape[0])
+                f = np.exp2(np.minimum(t // int(k_growth), 12)).astype(np.float32)
+                L.k[b] = (x * f[:, None, None]).astype(np.float32)
     if kv_dtype:
         if kv_dtype != "fp8" or wl.dtype != "bf16":
             raise ValueError("kv_dtype='fp8' needs a bf16 workload")

@@ -109,14 +109,16 @@ def test_partition_must_fit_the_kernel():
 
 
 def test_head_dim_512_limits():
-    # decode takes head_dim 512 over bf16 and FP8 pools, not float32; prefill does not take it
+    # head_dim 512 over bf16 and FP8 pools, not float32; no head_dim outside {64, 128, 256, 512}
     assert pk.paged_attn_decode_workspace_bytes(2, 4, 2, 512, 16, 100, 0, 32, "bf16") > 0
     with pytest.raises(pk.PagedError) as e:
         pk.paged_attn_decode_workspace_bytes(2, 4, 2, 512, 16, 100, 0, 32, "f32")
     assert e.value.code == pk.PAGED_ERR_INVALID_ARG
-    rc = pk.lib.paged_attn_prefill_chunk(None, None, None, None, None, 4, None, None, 1, 8, 8, 8, 8, 512,
-                                         16, 8, 0.1, 0, pk.PAGED_BF16, None)
-    assert rc == pk.PAGED_ERR_INVALID_ARG
+    for d in (96, 384, 1024):
+        rc = pk.lib.paged_attn_prefill_chunk(None, None, None, None, None, 4, None, None, 1, 8, 8, 8, 8, d,
+                                             16, 8, 0.1, 0, pk.PAGED_BF16, None)
+        assert rc == pk.PAGED_ERR_INVALID_ARG
+        assert b"head_dim" in pk.lib.paged_last_error()
     assert pk.lib.paged_kv_write(None, None, None, None, None, 1, 8, 16, 1, 1024, 1, None) == \
         pk.PAGED_ERR_INVALID_ARG
 
@@ -135,7 +137,7 @@ def test_mixed_step_argument_errors():
     assert call(B=0, nd=0, T=0) == pk.PAGED_OK              # nothing to do
     assert call() == pk.PAGED_ERR_INVALID_ARG               # NULL pointers
     # everything below is rejected before any device call
-    assert call(d=512, ptr=16) == pk.PAGED_ERR_INVALID_ARG  # chunk rows need head_dim <= 256
+    assert call(d=384, ptr=16) == pk.PAGED_ERR_INVALID_ARG  # no kernel for head_dim 384
     assert call(ptr=16, part=32) == pk.PAGED_ERR_CAPACITY   # two partitions: a workspace is needed
     assert b"workspace" in pk.lib.paged_last_error()
 

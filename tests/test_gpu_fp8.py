@@ -156,7 +156,9 @@ def test_fp8_decode_full_size(pk, name):
     dict(batch=2, context=[100, 64], chunk=[64, 100], num_blocks=64, hq=16, hkv=2, head_dim=64),
     dict(batch=2, context=[100, 64], chunk=[64, 100], num_blocks=64, hq=4, hkv=1, head_dim=256),
     dict(batch=2, context=[100, 37], chunk=[40, 20], num_blocks=64, block_size=8),
-], ids=[str(i) for i in range(5)])
+    dict(batch=2, context=[300, 64], chunk=[150, 100], num_blocks=64, hq=8, hkv=1, head_dim=512, window=37),
+    dict(batch=2, context=[100, 37], chunk=[40, 20], num_blocks=64, hq=4, hkv=2, head_dim=512, block_size=8),
+], ids=[str(i) for i in range(7)])
 def test_fp8_prefill_small(pk, kw):
     run_case(pk, synth.make("prefill", kv_dtype="fp8", **kw), label="fp8-prefill")
 

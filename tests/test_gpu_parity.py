@@ -360,6 +360,59 @@ def test_hybrid_prefill_full_size_sampled_rows(pk):
     run_case(pk, wl, rows=rows, label="hprefill-full")
 
 
+# head_dim 512 (full-attention layers of the Gemma-style models): 32-key K/V
+# tiles, four waves of 16 query rows per workgroup.
+PREFILL_D512 = [
+    ("prefill", dict(batch=3, context=[70, 33, 0], chunk=[40, 9, 17], num_blocks=64, hq=4, hkv=1, head_dim=512)),
+    ("prefill", dict(batch=2, context=[300, 64], chunk=[150, 100], num_blocks=64, hq=8, hkv=2, head_dim=512,
+                     window=37)),
+    ("prefill", dict(batch=2, context=[100, 37], chunk=[40, 20], num_blocks=64, hq=2, hkv=2, head_dim=512,
+                     block_size=8)),
+    ("prefill", dict(batch=2, context=[300, 5], chunk=[200, 130], num_blocks=64, hq=8, hkv=1, head_dim=512,
+                     block_size=64)),
+    ("prefill", dict(batch=1, context=[100], chunk=[64], num_blocks=64, hq=16, hkv=1, head_dim=512,
+                     block_size=32, window=45)),
+    ("hprefill", dict(batch=2, context=[300, 700], chunk=[100, 37], window=64, num_blocks=200,
+                      sliding_blocks=64, head_dim=512)),
+]
+
+
+@pytest.mark.parametrize("name,kw", PREFILL_D512, ids=[f"{n}-{i}" for i, (n, _) in enumerate(PREFILL_D512)])
+def test_prefill_head_dim_512(pk, name, kw):
+    run_case(pk, synth.make(name, **kw), label="prefill-d512")
+
+
+def test_hybrid_prefill_head_dim_512_full_size_sampled_rows(pk):
+    wl = synth.make("hprefill", head_dim=512)
+    T = int(wl.chunk_lens.sum())
+    rows = sorted(set([0, 1, 2, 2047, 2048, 4095, 4096, 6143, 6144, T - 2, T - 1] +
+                      list(np.random.default_rng(8).integers(0, T, size=25))))
+    run_case(pk, wl, rows=rows, label="hprefill-d512-full")
+
+
+# Keys scaled by 2^(position // 32): the running score maximum jumps by far
+# more than the kernels' rescale threshold every few tiles or stages, so the
+# online softmax rescales accumulators that already hold data.
+K_GROWTH = [
+    ("prefill", dict(batch=2, context=[300, 64], chunk=[150, 100], num_blocks=64)),
+    ("prefill", dict(batch=2, context=[100, 64], chunk=[64, 100], num_blocks=64, hq=16, hkv=2, head_dim=64)),
+    ("prefill", dict(batch=2, context=[300, 64], chunk=[150, 100], num_blocks=64, hq=4, hkv=1, head_dim=256)),
+    ("prefill", dict(batch=2, context=[300, 64], chunk=[150, 100], num_blocks=64, hq=8, hkv=1, head_dim=512)),
+    ("hprefill", dict(batch=2, context=[300, 700], chunk=[100, 37], window=64, num_blocks=200,
+                      sliding_blocks=64)),
+    ("qwen3", dict(context=500, prefix=64, num_blocks=200, part=128)),
+    ("mixed", dict(batch=5, context=(20, 900), prefix=100, num_blocks=300, part=64)),
+    ("hybrid", dict(batch=2, context=500, window=100, head_dim=512, sliding_blocks=60, num_blocks=100)),
+    ("tiny", dict()),
+    ("mixedstep", dict(batch=3, context=(100, 600), chunk=[77], prefix=[500], num_blocks=200, part=64)),
+]
+
+
+@pytest.mark.parametrize("name,kw", K_GROWTH, ids=[f"{n}-{i}" for i, (n, _) in enumerate(K_GROWTH)])
+def test_growing_scores_rescale(pk, name, kw):
+    run_case(pk, synth.make(name, k_growth=32, **kw), label="k-growth")
+
+
 # One continuous-batching step: decode rows (split-K decode kernels on the
 # caller's stream) and prefill chunks (prefill kernel on the side stream) in
 # one call, checked against the oracle's varlen prefill over all rows.
@@ -370,6 +423,8 @@ MIXED_STEP = [
     dict(batch=6, context=(1, 400), chunk=[33, 129], prefix=[64, 17], num_blocks=300, block_size=8, part=64),
     dict(batch=2, context=(300, 700), chunk=[100], prefix=[250], num_blocks=100, block_size=64, hq=8, hkv=1,
          head_dim=256, part=128),
+    dict(batch=3, context=(200, 600), chunk=[90], prefix=[150], num_blocks=200, hq=8, hkv=1, head_dim=512,
+         part=128),
     dict(batch=0, chunk=[120, 5], prefix=[30, 300], num_blocks=100),
     dict(batch=4, context=(10, 200), chunk=[], prefix=[], num_blocks=100, part=32),
 ]
