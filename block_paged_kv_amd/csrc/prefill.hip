@@ -294,18 +294,37 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
   typedef floatx4_t Scores[JT][NS];
   uint4 pa[JT][NK];  // P as bf16 A operands: [query tile][32-key step]
 
-  // ---- S^T = K Q^T, key sub-tiles t4 in [t0, t1) x 2 query tiles --------------
-  auto tile_s = [&](Scores& sc, const uint16_t* ks_buf, int t0, int t1) {
+  // ---- S^T = K Q^T over the tile's NS key sub-tiles x JT query tiles ----------
+  // The swizzle changes only the low four bits of a chunk index, so chunk
+  // 4ks + lg = 16 (ks / 4) + (4 (ks % 4) + lg) lands at 16 (ks / 4) plus one of
+  // four lane-dependent positions: the rest is an immediate offset.
+  // The K fragment reads run PF fragments ahead of the products and the key
+  // sub-tiles' accumulation chains alternate; scheduling barriers keep that
+  // order (left to itself the compiler waits on each read right before its
+  // product, which a second wave on the SIMD can only partly hide and, at
+  // head_dim 512 with one wave per SIMD, nothing hides).
+  auto tile_s = [&](Scores& sc, const uint16_t* ks_buf) {
+    const uint16_t* krow = ks_buf + lq * D;
+    auto kfrag = [&](int t4, int ks) {
+      const int pos = (((4 * (ks & 3) + lg) ^ swz_k(lq)) << 3) + (ks >> 2) * 128;
+      return *reinterpret_cast<const uint4*>(krow + t4 * 16 * D + pos);
+    };
+    constexpr int PF = 4;
+    constexpr int NR = NS * KS;  // K fragments of one tile; fragment u: sub-tile u % NS, step u / NS
+    uint4 kf[PF + 1];
 #pragma unroll
-    for (int t4 = t0; t4 < t1; ++t4) {
+    for (int t4 = 0; t4 < NS; ++t4)
 #pragma unroll
       for (int j = 0; j < JT; ++j) sc[j][t4] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const uint4 ka = *reinterpret_cast<const uint4*>(&ks_buf[(t4 * 16 + lq) * D + (((4 * ks + lg) ^ swz_k(lq)) << 3)]);
+    for (int u = 0; u < PF; ++u) kf[u] = kfrag(u % NS, u / NS);
 #pragma unroll
-        for (int j = 0; j < JT; ++j) sc[j][t4] = mfma16x16x32(ka, qreg[j][ks], sc[j][t4]);
-      }
+    for (int u = 0; u < NR; ++u) {
+      if (u + PF < NR) kf[(u + PF) % (PF + 1)] = kfrag((u + PF) % NS, (u + PF) / NS);
+#pragma unroll
+      for (int j = 0; j < JT; ++j)
+        sc[j][u % NS] = mfma16x16x32(kf[u % (PF + 1)], qreg[j][u / NS], sc[j][u % NS]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -417,7 +436,9 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
       const int vsw = swz_v(vrow);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const int vc = ((2 * nt + ((lq & 3) >> 1)) ^ vsw) << 3;
+        // Chunk 2nt + b = 16 (nt / 8) + (2 (nt % 8) + b); the swizzle (below 16)
+        // touches only the second part.
+        const int vc = (((2 * (nt & 7) + ((lq & 3) >> 1)) ^ vsw) << 3) + (nt >> 3) * 128;
         const uint2 v0 = ds_read_tr16(vbase + vc);
         const uint2 v1 = ds_read_tr16(vbase + 16 * D + vc);
         const uint4 vb = make_uint4(v0.x, v0.y, v1.x, v1.y);
@@ -450,7 +471,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
     }
     const int ts = kt * kTileN;
     __builtin_amdgcn_s_setprio(1);
-    tile_s(sc, k_s[buf], 0, NS);
+    tile_s(sc, k_s[buf]);
     __builtin_amdgcn_s_setprio(0);
     tile_softmax(sc, needs_mask(ts), ts, [] {});
     tile_pv(v_s[buf]);
