@@ -427,23 +427,56 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
   // element j%4 of the rows addressed by lanes 4k + j/4 (k = 0..3): lane j
   // addresses row key0 + j/4, columns 16nt + 4(j%4) .. +3.
   auto tile_pv = [&](const uint16_t* vs_buf) {
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-#pragma unroll
-      for (int j = 0; j < JT; ++j) lsum[j] = mfma16x16x32(pa[j][kk], ones, lsum[j]);
-      const int vrow = kk * 32 + 4 * lg + (lq >> 2);  // and vrow + 16: same swizzle
+    if constexpr (D >= 256) {
+      // The V fragment reads (fragment u: 32-key step u / NT, column tile
+      // u % NT) run PF fragments ahead of the products, as in tile_s; up to
+      // head_dim 128 the compiler's own order measured as fast.
+      const int vrow = 4 * lg + (lq >> 2);  // + 32 kk, and + 16: same swizzle
       const uint16_t* vbase = &vs_buf[vrow * D + 4 * (lq & 1)];
       const int vsw = swz_v(vrow);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        // Chunk 2nt + b = 16 (nt / 8) + (2 (nt % 8) + b); the swizzle (below 16)
-        // touches only the second part.
-        const int vc = (((2 * (nt & 7) + ((lq & 3) >> 1)) ^ vsw) << 3) + (nt >> 3) * 128;
+      auto vfrag = [&](int u) {
+        const int kk = u / NT, nt = u % NT;
+        const int vc = (((2 * (nt & 7) + ((lq & 3) >> 1)) ^ vsw) << 3) + (nt >> 3) * 128 + kk * 32 * D;
         const uint2 v0 = ds_read_tr16(vbase + vc);
         const uint2 v1 = ds_read_tr16(vbase + 16 * D + vc);
-        const uint4 vb = make_uint4(v0.x, v0.y, v1.x, v1.y);
+        return make_uint4(v0.x, v0.y, v1.x, v1.y);
+      };
+      constexpr int PF = 4;
+      constexpr int NV = NK * NT;
+      uint4 vf[PF + 1];
 #pragma unroll
-        for (int j = 0; j < JT; ++j) o[j][nt] = mfma16x16x32(pa[j][kk], vb, o[j][nt]);
+      for (int u = 0; u < PF; ++u) vf[u] = vfrag(u);
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        if (u + PF < NV) vf[(u + PF) % (PF + 1)] = vfrag(u + PF);
+        const int kk = u / NT, nt = u % NT;
+        if (nt == 0) {
+#pragma unroll
+          for (int j = 0; j < JT; ++j) lsum[j] = mfma16x16x32(pa[j][kk], ones, lsum[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < JT; ++j) o[j][nt] = mfma16x16x32(pa[j][kk], vf[u % (PF + 1)], o[j][nt]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+#pragma unroll
+        for (int j = 0; j < JT; ++j) lsum[j] = mfma16x16x32(pa[j][kk], ones, lsum[j]);
+        const int vrow = kk * 32 + 4 * lg + (lq >> 2);  // and vrow + 16: same swizzle
+        const uint16_t* vbase = &vs_buf[vrow * D + 4 * (lq & 1)];
+        const int vsw = swz_v(vrow);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          // Chunk 2nt + b = 16 (nt / 8) + (2 (nt % 8) + b); the swizzle (below 16)
+          // touches only the second part.
+          const int vc = (((2 * (nt & 7) + ((lq & 3) >> 1)) ^ vsw) << 3) + (nt >> 3) * 128;
+          const uint2 v0 = ds_read_tr16(vbase + vc);
+          const uint2 v1 = ds_read_tr16(vbase + 16 * D + vc);
+          const uint4 vb = make_uint4(v0.x, v0.y, v1.x, v1.y);
+#pragma unroll
+          for (int j = 0; j < JT; ++j) o[j][nt] = mfma16x16x32(pa[j][kk], vb, o[j][nt]);
+        }
       }
     }
   };
