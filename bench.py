@@ -124,7 +124,7 @@ def counter_traffic(kern, workload):
     """HBM bytes per launch recorded in profiles/<kern>_<workload>_hbm_counters.md
     (FETCH_SIZE and WRITE_SIZE, scaled by a copy of known size), or None when
     the file is missing or the kernel source changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"{kern}_{workload}_hbm_counters.md")
+    path = os.path.join(ROOT, "profiles", f"{kern}_{workload}_hbm_counters.md")  # workload: name[_dD][_fp8]
     if not os.path.exists(path):
         return None
     fields = {}
@@ -547,7 +547,8 @@ def main():
             "peak": peak,
             "unit": runit,
             "frac": round(achieved / peak, 4),
-            "traffic": counter_traffic(kern, args.workload + ("_fp8" if fp8 else "")),
+            "traffic": counter_traffic(kern, args.workload + (f"_d{args.head_dim}" if args.head_dim else "")
+                                       + ("_fp8" if fp8 else "")),
             "avg_launch_us": round(k_ms * 1e3 / max(k_n, 1), 3),
             "launch_us_p10_p50_p90": launch_percentiles(pk, kern),
             "launches": k_n,
