@@ -123,6 +123,17 @@ def test_head_dim_512_limits():
         pk.PAGED_ERR_INVALID_ARG
 
 
+def test_partition_count_limit():
+    # at most 65535 partitions (the grid's z dimension): rejected before any device call
+    L = pk.lib
+    rc = L.paged_attn_decode(None, None, None, None, None, 4, None, 2, 4, 2, 128, 16, 8, 0.1, 0, 16,
+                             65536 * 16, None, 0, pk.PAGED_BF16, None)
+    assert rc == pk.PAGED_ERR_INVALID_ARG
+    assert b"65535" in L.paged_last_error()
+    assert pk.paged_attn_decode_workspace_bytes(2, 4, 2, 128, 16, 65535 * 16, 0, 16, "bf16") == \
+        2 * 4 * 65535 * (128 + 2) * 4
+
+
 def test_mixed_step_argument_errors():
     L = pk.lib
 

@@ -245,6 +245,33 @@ def test_decode_edge_lengths(pk):
              partition_tokens=16)
 
 
+# ------------------------------------------------------------ maximum sizes
+def test_decode_long_row(pk):
+    # one 131072-token row (8192 blocks of one KV head, 8 query heads), the
+    # library's partition rule
+    run_case(pk, synth.make("qwen3", batch=1, context=131072, prefix=0, hq=8, hkv=1, num_blocks=8200),
+             label="decode-128k")
+
+
+def test_decode_partition_limit(pk):
+    # 65535 partitions of 16 tokens (the grid's z limit): all but the first few
+    # of every row are empty
+    wl = synth.make("mixed", batch=2, context=(100, 300), prefix=32, hq=4, hkv=2, num_blocks=100)
+    run_case(pk, wl, label="decode-65535-parts", partition_tokens=16, max_seq_len=65535 * 16)
+
+
+def test_decode_large_batch(pk):
+    run_case(pk, synth.make("mixed", batch=1024, context=(1, 64), prefix=16, hq=8, hkv=4, num_blocks=5000),
+             label="decode-b1024")
+
+
+def test_prefill_long_chunk_sampled_rows(pk):
+    wl = synth.make("prefill", batch=1, context=[4096], chunk=[8192], num_blocks=800)
+    rows = sorted(set([0, 1, 255, 256, 4095, 4096, 8190, 8191] +
+                      list(np.random.default_rng(9).integers(0, 8192, size=24))))
+    run_case(pk, wl, rows=rows, label="prefill-8k-chunk")
+
+
 def test_decode_empty_row_gives_zeros(pk):
     import torch
 
