@@ -9,10 +9,13 @@
 // How (ours):
 //   * Query rows are (position, query head) pairs of one KV head, packed
 //     position-major, so the G query heads sharing a KV head share every K/V
-//     tile. A workgroup of 4 waves owns 128 rows; each wave owns 32.
-//   * K/V tiles of 64 keys (whole blocks) are staged in LDS, both row-major
-//     (key, head_dim); the P.V operand is read with a transposing LDS read
-//     (ds_read_b64_tr_b16), which hands each lane consecutive keys.
+//     tile. A wave owns 32 rows up to head_dim 128 and 16 beyond; a
+//     workgroup has eight waves (four at head_dim 512, and inside the mixed
+//     step).
+//   * K/V tiles of 64 keys (32 at head_dim 512) are staged in LDS, both
+//     row-major (key, head_dim); the P.V operand is read with a transposing
+//     LDS read (ds_read_b64_tr_b16), which hands each lane consecutive keys.
+//     Operand reads run a few fragments ahead of the products.
 //   * S^T = K Q^T and O += P V run on v_mfma_f32_16x16x32_bf16 with fp32
 //     accumulators; the S^T accumulator layout (one query per lane, 4 keys per
 //     register group) is exactly the A-operand layout P needs, once converted
