@@ -109,14 +109,26 @@ def prefill_flops(wl, rows=None):
     return 4.0 * wl.head_dim * wl.hq * pairs
 
 
+def code_lines(text):
+    """A source's code without its // comments, blank lines and indentation
+    (the kernel's identity for recorded counters: editing a comment does not
+    change the kernel)."""
+    out = []
+    for line in text.splitlines():
+        code = line.split("//", 1)[0].strip()
+        if code:
+            out.append(code)
+    return "\n".join(out)
+
+
 def source_hash(kern):
-    """sha256 of the source files a kernel is built from."""
+    """sha256 of the code of the source files a kernel is built from."""
     import hashlib
 
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kern]:
-        with open(os.path.join(ROOT, "block_paged_kv_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "block_paged_kv_amd", "csrc", f)) as fh:
+            h.update(code_lines(fh.read()).encode())
     return h.hexdigest()
 
 
