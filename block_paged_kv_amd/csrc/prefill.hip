@@ -27,7 +27,6 @@
 //     then serves the head's K/V to all of its tiles.
 
 #include <cmath>
-#include <type_traits>
 
 #include "attn.h"
 #include "device.h"
@@ -333,9 +332,8 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
 
   // ---- online softmax (lane: query 16j+lq, keys ts + 16*t4 + 4*lg + i) --------
   // Tiles that lie wholly inside every row's [lo, a] range skip the mask. The
-  // probabilities are produced in 32-key steps (keys 0-31, then 32-63 of a
-  // 64-key tile); `mid` runs between the two.
-  auto tile_softmax = [&](Scores& sc, bool need_mask, int ts, auto&& mid) {
+  // probabilities are produced in 32-key steps, one P operand per step.
+  auto tile_softmax = [&](Scores& sc, bool need_mask, int ts) {
     if (need_mask) {
       // Rows past the tile's last row keep their (zero-query) scores: their
       // outputs are never stored. The empty asm makes the bounds opaque so
@@ -407,7 +405,6 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
     }
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
-      if (kk == 1) mid();
 #pragma unroll
       for (int j = 0; j < JT; ++j) {
         float pr[2][4];
@@ -509,7 +506,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
     __builtin_amdgcn_s_setprio(1);
     tile_s(sc, k_s[buf]);
     __builtin_amdgcn_s_setprio(0);
-    tile_softmax(sc, needs_mask(ts), ts, [] {});
+    tile_softmax(sc, needs_mask(ts), ts);
     tile_pv(v_s[buf]);
     if (has_next) stage_store(buf ^ 1);
     __syncthreads();
