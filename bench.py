@@ -19,11 +19,14 @@ library on the launch stream over the timed region) and the CPU oracle's rate
 on a bounded sample of the same workload.
 
     python bench.py [--workload qwen3|mixed|hybrid|prefill|hprefill|mixedstep|tiny] [--kv bf16|fp8]
-                    [--steps K] [--warmup W]
+                    [--head-dim D] [--scrub] [--steps K] [--warmup W]
 
 ``--kv fp8`` runs the same workload over FP8 (E4M3) pools with per-layer
 scales (quantizing write, FP8 decode/prefill); the decode byte count then
-counts one byte per K/V element.
+counts one byte per K/V element. ``--head-dim`` changes the workload's head
+dimension (e.g. 512 for the Gemma-style hybrid decode or prefill).
+``--scrub`` reads 1 GiB before every timed attention launch, so the
+per-kernel times are taken with caches holding unrelated data.
 """
 
 from __future__ import annotations
