@@ -58,3 +58,29 @@ def test_hybrid_prefill_shapes():
     assert wl.chunk_lens.tolist() == [2048] * 4 and wl.seq_lens.tolist() == [8192] * 4
     assert [L.name for L in wl.layers] == ["sliding", "full", "shared"]
     assert wl.layer("sliding").window == 512 and wl.layer("shared").alias_of == "full"
+
+
+def test_growing_keys_are_exact_powers_of_two_of_the_plain_draws():
+    # k_growth scales the key at position t by 2^min(t // g, 12) and changes nothing else
+    for name, kw in [("prefill", dict(batch=2, context=[300, 64], chunk=[150, 100], num_blocks=64)),
+                     ("mixed", dict(batch=3, context=(20, 400), prefix=100, num_blocks=100)),
+                     ("hprefill", dict(batch=2, context=[300, 700], chunk=[100, 37], window=64,
+                                       num_blocks=200, sliding_blocks=64))]:
+        a = synth.make(name, **kw)
+        g = synth.make(name, k_growth=32, **kw)
+        for La, Lg in zip(a.layers, g.layers):
+            if La.alias_of:
+                assert Lg.alias_of == La.alias_of
+                continue
+            np.testing.assert_array_equal(La.q, Lg.q)
+            for xa, xg, va, vg, lf in zip(La.k, Lg.k, La.v, Lg.v, La.live_from):
+                np.testing.assert_array_equal(va, vg)
+                f = np.exp2(np.minimum((lf + np.arange(len(xa))) // 32, 12)).astype(np.float32)
+                np.testing.assert_array_equal(xg, xa * f[:, None, None])
+    # the largest score of a long row does grow past the kernels' rescale threshold (2^8)
+    wl = synth.make("prefill", batch=1, context=[300], chunk=[100], num_blocks=64, k_growth=32)
+    k = wl.layers[0].k[0][:, 0].astype(np.float64)
+    q = wl.layers[0].q[-1, 0].astype(np.float64)
+    s = wl.scale * (k @ q) / np.log(2.0)
+    running = np.maximum.accumulate(s)
+    assert np.count_nonzero(np.diff(running) > 8.0) >= 2
