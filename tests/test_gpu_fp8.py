@@ -186,3 +186,15 @@ def test_plain_entry_points_reject_fp8_pools(pk):
     assert rc == pk.PAGED_ERR_DTYPE
     with pytest.raises(pk.PagedError):
         pk.paged_attn_decode_fp8(out, q, kp, kp, bt, sl, 0.1, 0.0, 1.0, 64)  # k_scale must be > 0
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("prefill", dict(batch=2, context=[300, 64], chunk=[150, 100], num_blocks=64)),
+    ("prefill", dict(batch=2, context=[300, 64], chunk=[150, 100], num_blocks=64, hq=8, hkv=1, head_dim=512)),
+    ("mixed", dict(batch=5, context=(20, 900), prefix=100, num_blocks=300, part=64)),
+    ("hybrid", dict(batch=2, context=500, window=100, head_dim=256, sliding_blocks=60, num_blocks=100)),
+], ids=["prefill", "prefill-d512", "mixed", "hybrid"])
+def test_fp8_growing_scores_rescale(pk, name, kw):
+    # keys scaled by 2^(position // 32): the online softmax over FP8 codes
+    # rescales accumulators that already hold data
+    run_case(pk, synth.make(name, kv_dtype="fp8", k_growth=32, **kw), label="fp8-k-growth")
