@@ -159,3 +159,79 @@ def test_request_lifecycle_prefix_reuse_grow_and_eviction(pk):
     both("commit_tokens", 4, tok_d[64:])
     logical[4] = (kd, vd)
     check([2, 4])
+
+
+@pytest.mark.gpu
+def test_continuous_batching_steps(pk):
+    # Two requests served over five steps with paged_attn_mixed: X's 150-token
+    # prompt in chunks of 64, 64 and 22 while Y (a 40-token prompt, one chunk)
+    # decodes beside it; then both decode. Each step reserves and writes its
+    # new tokens' K/V (allocator slots, paged_kv_write) before attention, and
+    # every query of the step is checked against attention over the request's
+    # logical K/V up to its own position.
+    import torch
+
+    announce("continuous batching over five steps")
+    rng = np.random.default_rng(1008)
+    scale = 1.0 / np.sqrt(D)
+    dev = torch.device("cuda")
+    order = [int(x) for x in rng.permutation(np.arange(1, 40))]
+    cpp = pk.Allocator(40, BS, order)
+    ref = RefAllocator(40, BS, order)
+    pools = {n: torch.zeros((40, HKV, BS, D), dtype=torch.bfloat16, device=dev) for n in "kv"}
+    k_log = {1: np.zeros((0, HKV, D), np.float32), 2: np.zeros((0, HKV, D), np.float32)}
+    v_log = {1: k_log[1].copy(), 2: k_log[2].copy()}
+    for s in (1, 2):
+        cpp.add(s)
+        ref.add(s)
+    # (request, new tokens) per step, decode rows first
+    steps = [[(2, 40), (1, 64)], [(2, 1), (1, 64)], [(2, 1), (1, 22)], [(2, 1), (1, 1)], [(1, 1), (2, 1)]]
+    next_tok = {1: 10_000, 2: 20_000}
+    for i, rows in enumerate(steps):
+        nd = sum(1 for s, c in rows if c == 1 and cpp.num_tokens(s) > 0)
+        starts, qs = [], []
+        for s, c in rows:
+            start = cpp.num_tokens(s)
+            assert start == ref.num_tokens(s)
+            for alloc in (cpp, ref):
+                alloc.reserve(s, start + c)
+            k_new = synth.round_bf16(rng.standard_normal((c, HKV, D), dtype=np.float32))
+            v_new = synth.round_bf16(rng.standard_normal((c, HKV, D), dtype=np.float32))
+            slots = cpp.slot_mapping(s, start, c)
+            assert list(slots) == list(ref.slot_mapping(s, start, c))
+            t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(torch.bfloat16)  # noqa: E731
+            pk.paged_kv_write(pools["k"], pools["v"], t(k_new), t(v_new), torch.from_numpy(slots).to(dev))
+            toks = list(range(next_tok[s], next_tok[s] + c))
+            next_tok[s] += c
+            for alloc in (cpp, ref):
+                alloc.commit_tokens(s, toks)
+            k_log[s] = np.concatenate([k_log[s], k_new])
+            v_log[s] = np.concatenate([v_log[s], v_new])
+            starts.append(start)
+            qs.append(synth.round_bf16(rng.standard_normal((c, HQ, D), dtype=np.float32)))
+        seqs = [s for s, _ in rows]
+        counts = [c for _, c in rows]
+        lens = [cpp.num_tokens(s) for s in seqs]
+        mb = max(cpp.num_blocks_of(s) for s in seqs)
+        tab = cpp.block_tables(seqs, mb)
+        assert [list(r) for r in tab] == [list(r) for r in ref.block_tables(seqs, mb)]
+        q = np.concatenate(qs)
+        cu = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+        msl = max(lens)
+        need = pk.paged_attn_decode_workspace_bytes(max(nd, 1), HQ, HKV, D, BS, msl, 0, 0, "bf16")
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        out = torch.empty((int(cu[-1]), HQ, D), dtype=torch.bfloat16, device=dev)
+        pk.paged_attn_mixed(out, torch.from_numpy(q).to(dev).to(torch.bfloat16), pools["k"], pools["v"],
+                            torch.from_numpy(tab).to(dev), torch.from_numpy(cu).to(dev),
+                            torch.tensor(lens, dtype=torch.int32, device=dev), nd,
+                            max(c for _, c in rows), scale, msl, workspace=ws)
+        torch.cuda.synchronize()
+        exp = np.zeros((int(cu[-1]), HQ, D))
+        for r, (s, c) in enumerate(rows):
+            for j in range(c):
+                a = starts[r] + j  # absolute position of this query
+                for h in range(HQ):
+                    g = h // (HQ // HKV)
+                    exp[cu[r] + j, h] = attend_one(q[cu[r] + j, h], k_log[s][:a + 1, g], v_log[s][:a + 1, g], scale)
+        max_abs, rel = runner.compare(out, exp, "bf16")
+        assert runner.within("bf16", max_abs, rel), (i, max_abs, rel)
