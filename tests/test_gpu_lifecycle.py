@@ -162,24 +162,32 @@ def test_request_lifecycle_prefix_reuse_grow_and_eviction(pk):
 
 
 @pytest.mark.gpu
-def test_continuous_batching_steps(pk):
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_continuous_batching_steps(pk, kv):
     # Two requests served over five steps with paged_attn_mixed: X's 150-token
     # prompt in chunks of 64, 64 and 22 while Y (a 40-token prompt, one chunk)
     # decodes beside it; then both decode. Each step reserves and writes its
     # new tokens' K/V (allocator slots, paged_kv_write) before attention, and
     # every query of the step is checked against attention over the request's
-    # logical K/V up to its own position.
+    # logical K/V up to its own position. Over FP8 pools the logical K/V are
+    # the values the codes stand for (the oracle's quantizer, then scale x
+    # code).
     import torch
 
-    announce("continuous batching over five steps")
+    from oracle import fp8 as ofp8
+
+    announce(f"continuous batching over five steps ({kv})")
+    fp8 = kv == "fp8"
+    ks, vs = (np.float32(4.0 / 448), np.float32(3.5 / 448)) if fp8 else (1.0, 1.0)
     rng = np.random.default_rng(1008)
     scale = 1.0 / np.sqrt(D)
     dev = torch.device("cuda")
     order = [int(x) for x in rng.permutation(np.arange(1, 40))]
     cpp = pk.Allocator(40, BS, order)
     ref = RefAllocator(40, BS, order)
-    pools = {n: torch.zeros((40, HKV, BS, D), dtype=torch.bfloat16, device=dev) for n in "kv"}
-    k_log = {1: np.zeros((0, HKV, D), np.float32), 2: np.zeros((0, HKV, D), np.float32)}
+    pdt = torch.float8_e4m3fn if fp8 else torch.bfloat16
+    pools = {n: torch.zeros((40, HKV, BS, D), dtype=pdt, device=dev) for n in "kv"}
+    k_log = {1: np.zeros((0, HKV, D)), 2: np.zeros((0, HKV, D))}
     v_log = {1: k_log[1].copy(), 2: k_log[2].copy()}
     for s in (1, 2):
         cpp.add(s)
@@ -200,7 +208,13 @@ def test_continuous_batching_steps(pk):
             slots = cpp.slot_mapping(s, start, c)
             assert list(slots) == list(ref.slot_mapping(s, start, c))
             t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(torch.bfloat16)  # noqa: E731
-            pk.paged_kv_write(pools["k"], pools["v"], t(k_new), t(v_new), torch.from_numpy(slots).to(dev))
+            if fp8:
+                pk.paged_kv_write_fp8(pools["k"], pools["v"], t(k_new), t(v_new), torch.from_numpy(slots).to(dev),
+                                      float(ks), float(vs))
+                k_new = ofp8.dequantize(ofp8.quantize(k_new, ks), ks)
+                v_new = ofp8.dequantize(ofp8.quantize(v_new, vs), vs)
+            else:
+                pk.paged_kv_write(pools["k"], pools["v"], t(k_new), t(v_new), torch.from_numpy(slots).to(dev))
             toks = list(range(next_tok[s], next_tok[s] + c))
             next_tok[s] += c
             for alloc in (cpp, ref):
@@ -218,13 +232,14 @@ def test_continuous_batching_steps(pk):
         q = np.concatenate(qs)
         cu = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
         msl = max(lens)
-        need = pk.paged_attn_decode_workspace_bytes(max(nd, 1), HQ, HKV, D, BS, msl, 0, 0, "bf16")
+        need = pk.paged_attn_decode_workspace_bytes(max(nd, 1), HQ, HKV, D, BS, msl, 0, 0, kv)
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
         out = torch.empty((int(cu[-1]), HQ, D), dtype=torch.bfloat16, device=dev)
         pk.paged_attn_mixed(out, torch.from_numpy(q).to(dev).to(torch.bfloat16), pools["k"], pools["v"],
                             torch.from_numpy(tab).to(dev), torch.from_numpy(cu).to(dev),
                             torch.tensor(lens, dtype=torch.int32, device=dev), nd,
-                            max(c for _, c in rows), scale, msl, workspace=ws)
+                            max(c for _, c in rows), scale, msl, workspace=ws, k_scale=float(ks),
+                            v_scale=float(vs))
         torch.cuda.synchronize()
         exp = np.zeros((int(cu[-1]), HQ, D))
         for r, (s, c) in enumerate(rows):
