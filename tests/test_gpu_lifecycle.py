@@ -162,8 +162,8 @@ def test_request_lifecycle_prefix_reuse_grow_and_eviction(pk):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("kv", ["bf16", "fp8"])
-def test_continuous_batching_steps(pk, kv):
+@pytest.mark.parametrize("kv,window", [("bf16", 0), ("fp8", 0), ("bf16", 48)])
+def test_continuous_batching_steps(pk, kv, window):
     # Two requests served over five steps with paged_attn_mixed: X's 150-token
     # prompt in chunks of 64, 64 and 22 while Y (a 40-token prompt, one chunk)
     # decodes beside it; then both decode. Each step reserves and writes its
@@ -171,12 +171,14 @@ def test_continuous_batching_steps(pk, kv):
     # every query of the step is checked against attention over the request's
     # logical K/V up to its own position. Over FP8 pools the logical K/V are
     # the values the codes stand for (the oracle's quantizer, then scale x
-    # code).
+    # code). With a sliding window every request drops its blocks that fell
+    # out of the window before a step commits new tokens (null table entries
+    # the kernels must skip).
     import torch
 
     from oracle import fp8 as ofp8
 
-    announce(f"continuous batching over five steps ({kv})")
+    announce(f"continuous batching over five steps ({kv}, window {window})")
     fp8 = kv == "fp8"
     ks, vs = (np.float32(4.0 / 448), np.float32(3.5 / 448)) if fp8 else (1.0, 1.0)
     rng = np.random.default_rng(1008)
@@ -201,6 +203,9 @@ def test_continuous_batching_steps(pk, kv):
         for s, c in rows:
             start = cpp.num_tokens(s)
             assert start == ref.num_tokens(s)
+            if window:
+                for alloc in (cpp, ref):
+                    alloc.drop_outside_window(s, window)
             for alloc in (cpp, ref):
                 alloc.reserve(s, start + c)
             k_new = synth.round_bf16(rng.standard_normal((c, HKV, D), dtype=np.float32))
@@ -232,21 +237,26 @@ def test_continuous_batching_steps(pk, kv):
         q = np.concatenate(qs)
         cu = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
         msl = max(lens)
-        need = pk.paged_attn_decode_workspace_bytes(max(nd, 1), HQ, HKV, D, BS, msl, 0, 0, kv)
+        need = pk.paged_attn_decode_workspace_bytes(max(nd, 1), HQ, HKV, D, BS, msl, window, 0, kv)
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
         out = torch.empty((int(cu[-1]), HQ, D), dtype=torch.bfloat16, device=dev)
         pk.paged_attn_mixed(out, torch.from_numpy(q).to(dev).to(torch.bfloat16), pools["k"], pools["v"],
                             torch.from_numpy(tab).to(dev), torch.from_numpy(cu).to(dev),
                             torch.tensor(lens, dtype=torch.int32, device=dev), nd,
-                            max(c for _, c in rows), scale, msl, workspace=ws, k_scale=float(ks),
-                            v_scale=float(vs))
+                            max(c for _, c in rows), scale, msl, sliding_window=window, workspace=ws,
+                            k_scale=float(ks), v_scale=float(vs))
         torch.cuda.synchronize()
         exp = np.zeros((int(cu[-1]), HQ, D))
         for r, (s, c) in enumerate(rows):
             for j in range(c):
                 a = starts[r] + j  # absolute position of this query
+                lo = max(0, a - window + 1) if window else 0
                 for h in range(HQ):
                     g = h // (HQ // HKV)
-                    exp[cu[r] + j, h] = attend_one(q[cu[r] + j, h], k_log[s][:a + 1, g], v_log[s][:a + 1, g], scale)
+                    exp[cu[r] + j, h] = attend_one(q[cu[r] + j, h], k_log[s][lo:a + 1, g], v_log[s][lo:a + 1, g],
+                                                   scale)
         max_abs, rel = runner.compare(out, exp, "bf16")
         assert runner.within("bf16", max_abs, rel), (i, max_abs, rel)
+        if window and i >= 1:
+            # the chunked request's first block expired and is a null entry
+            assert tab[seqs.index(1)][0] == 0
