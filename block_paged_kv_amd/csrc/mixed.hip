@@ -70,8 +70,10 @@ extern "C" int32_t paged_attn_mixed(void* out, const void* q, const void* k_pool
   SideStream side(s);
   if (side.status() != PAGED_OK) return side.status();
   // Chunk rows first (the long kernel starts first), on the side stream: their
-  // cu_q_lens entries are absolute offsets into q and out. Four-wave prefill
-  // workgroups leave a CU room for decode workgroups beside them.
+  // cu_q_lens entries are absolute offsets into q and out. The prefill runs
+  // four-wave workgroups, two per CU: once one of them finishes, decode
+  // workgroups fit beside the other (an eight-wave workgroup would hold its
+  // CU's registers until the end).
   int32_t rc = prefill_impl(out, q, k_pool, v_pool, block_tables + static_cast<size_t>(nd) * max_blocks_per_seq,
                             max_blocks_per_seq, cu_q_lens + nd, seq_lens + nd, np, total_q - nd,
                             max_q_len, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
