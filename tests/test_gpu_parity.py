@@ -462,9 +462,13 @@ def test_mixed_step_small(pk, kw):
     run_case(pk, synth.make("mixedstep", **kw), label="mixed-step")
 
 
-def test_mixed_step_fp8(pk):
-    run_case(pk, synth.make("mixedstep", batch=5, context=(20, 900), chunk=[150, 64], prefix=[300, 0],
-                            num_blocks=200, part=128, kv_dtype="fp8"), label="mixed-step-fp8")
+@pytest.mark.parametrize("kw", [
+    dict(batch=5, context=(20, 900), chunk=[150, 64], prefix=[300, 0], num_blocks=200, part=128),
+    dict(batch=3, context=(200, 600), chunk=[90, 33], prefix=[150, 70], num_blocks=200, hq=8, hkv=1,
+         head_dim=512, part=128),
+], ids=["d128", "d512"])
+def test_mixed_step_fp8(pk, kw):
+    run_case(pk, synth.make("mixedstep", kv_dtype="fp8", **kw), label="mixed-step-fp8")
 
 
 def test_mixed_step_full_size_sampled_rows(pk):
