@@ -169,3 +169,44 @@ def test_trace_api_without_launches():
     with pytest.raises(KeyError):
         pk.trace_query("nope")
     assert pk.lib.paged_trace_query(9, None, None) == pk.PAGED_ERR_INVALID_ARG
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    # A C99 program using only the header and the library (no Python, no
+    # torch): the host allocator through the ABI, from create to destroy.
+    import shutil
+    import subprocess
+
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "abi.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include "pagedkv.h"
+int main(void) {
+  paged_alloc* a = NULL;
+  int32_t table[4] = {0}, needed = 0, nb = 0;
+  int64_t seq = 7, slots[20];
+  if (paged_alloc_create(8, 16, NULL, &a) != PAGED_OK) return 1;
+  if (paged_seq_add(a, seq) != PAGED_OK) return 2;
+  if (paged_seq_reserve(a, seq, 20) != PAGED_OK) return 3;
+  if (paged_alloc_block_tables(a, &seq, 1, 4, table, &needed) != PAGED_OK) return 4;
+  if (paged_alloc_slot_mapping(a, seq, 0, 20, slots) != PAGED_OK) return 5;
+  if (paged_seq_reserve(a, seq, 16 * 8) != PAGED_ERR_NO_BLOCKS) return 6;
+  paged_alloc_num_blocks(a, &nb);
+  printf("%d %d %d %d %lld %lld\n", paged_abi_version(), nb, table[0], table[1],
+         (long long)slots[0], (long long)slots[19]);
+  return paged_alloc_destroy(a) == PAGED_OK ? 0 : 7;
+}
+''')
+    exe = tmp_path / "abi"
+    lib_dir = os.path.dirname(pk.LIB_PATH)
+    subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    str(src), "-L", lib_dir, "-lpagedkv", f"-Wl,-rpath,{lib_dir}", "-o", str(exe)], check=True)
+    run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert run.returncode == 0, (run.returncode, run.stderr)
+    ver, nb, b0, b1, s0, s19 = (int(x) for x in run.stdout.split())
+    assert ver == pk.abi_version() and nb == 8
+    # blocks 1..7 in ascending order without a free-list permutation; slots follow the table
+    assert (b0, b1) == (1, 2) and s0 == b0 * 16 and s19 == b1 * 16 + 3
