@@ -507,8 +507,15 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
     tile_s(sc, k_s[buf]);
     __builtin_amdgcn_s_setprio(0);
     tile_softmax(sc, needs_mask(ts), ts);
+    // FP8 codes up to head_dim 128 are widened into the other buffer before
+    // the P.V part, so the LDS stores drain under it rather than before the
+    // barrier (their loads have landed by then; measured 5% faster, and no
+    // faster at head_dim 256 and 512). Direct copies (bf16) only need their
+    // wait, as late as possible.
+    constexpr bool kEarlyStore = ESZ == 1 && D <= 128;
+    if (kEarlyStore && has_next) stage_store(buf ^ 1);
     tile_pv(v_s[buf]);
-    if (has_next) stage_store(buf ^ 1);
+    if (!kEarlyStore && has_next) stage_store(buf ^ 1);
     __syncthreads();
   }
 
