@@ -500,6 +500,9 @@ def test_prefill_chunk_of_one_matches_decode(pk):
     ("prefill", dict(batch=2, context=[300, 64], chunk=[150, 100], num_blocks=64)),
     ("mixedstep", dict(batch=5, context=(20, 900), chunk=[150, 64], prefix=[300, 0], num_blocks=200,
                        part=128)),
+    ("prefill", dict(batch=2, context=[300, 64], chunk=[150, 100], num_blocks=64, hq=8, hkv=1, head_dim=512)),
+    ("mixedstep", dict(batch=3, context=(200, 600), chunk=[90], prefix=[150], num_blocks=200, hq=8, hkv=1,
+                       head_dim=512, part=128)),
 ])
 def test_step_graph_replays_match_eager(pk, name, kw):
     """The step (KV write + attention) captured in a HIP graph, with the
