@@ -314,6 +314,38 @@ def pin_prefill_brute_force_two_rows():
             row += 1
 
 
+def pin_prefill_blocked_query_rows():
+    """Query blocking and the query_rows subset: with blocks of 3 rows (and with
+    the default 256-row blocks over a 300-row chunk), every computed row equals
+    scalar brute force on its own flat K/V span [lo, P+i], and rows outside the
+    subset are left NaN."""
+    rng = np.random.default_rng(25)
+    bs, hkv, hq, d = 4, 1, 2, 3
+    for P, C, window, q_block, rows in ((13, 10, 0, 3, [0, 2, 3, 5, 7, 8, 9]),
+                                        (13, 10, 5, 3, [1, 4, 6, 9]),
+                                        (7, 300, 0, 256, [0, 1, 255, 256, 257, 299]),
+                                        (7, 300, 9, 256, [3, 254, 256, 298])):
+        L = P + C
+        nblk = -(-L // bs)
+        nb = nblk + 3
+        table = list(rng.permutation(np.arange(1, nb))[:nblk])
+        fk = rng.normal(size=(L, hkv, d))
+        fv = rng.normal(size=(L, hkv, d))
+        kp, vp = scatter_flat(fk, fv, table, nb, bs)
+        q = rng.normal(size=(C, hq, d))
+        out = oracle.prefill_chunk(q, kp, vp, np.array([table]), [0, C], [L], 0.6, window, bs,
+                                   query_rows=rows, q_block=q_block)
+        for i in range(C):
+            if i not in rows:
+                assert np.all(np.isnan(out[i])), f"row {i} outside the subset was computed"
+                continue
+            a = P + i
+            lo = max(0, a - window + 1) if window else 0
+            for h in range(hq):
+                ref = brute_force(q[i, h], fk[lo:a + 1, 0], fv[lo:a + 1, 0], 0.6)
+                np.testing.assert_allclose(out[i, h], ref, atol=1e-12, err_msg=f"row {i} head {h}")
+
+
 def pin_pool_block_bytes():
     """mlx-node paged-cache doc, cold-tier writer table: a qwen3-0.6b block is
     1.84 MB. With that model's public geometry (28 layers, 8 KV heads, head_dim
@@ -406,6 +438,40 @@ def _mut_write_skips_last(k_pool, v_pool, new_k, new_v, slot_mapping, block_size
 
 _orig_write = A.kv_write
 MUTANTS["write drops the last token"] = ("kv_write", _mut_write_skips_last)
+
+
+def _prefill_variant(shift_later_blocks=0, subset_index=False):
+    """prefill_chunk with a blocking slip: rows of every block after the first
+    shifted by ``shift_later_blocks`` positions, or each row's position taken
+    from its index inside the query_rows subset instead of the chunk."""
+    def f(q, k_pool, v_pool, block_tables, cu_q_lens, seq_lens, scale, window, block_size,
+          query_rows=None, q_block=256):
+        q = np.asarray(q, dtype=np.float64)
+        T, Hq, D = q.shape
+        group = Hq // k_pool.shape[1]
+        out = np.full((T, Hq, D), np.nan)
+        wanted = None if query_rows is None else set(int(r) for r in query_rows)
+        for b in range(len(seq_lens)):
+            r0, r1 = int(cu_q_lens[b]), int(cu_q_lens[b + 1])
+            P = int(seq_lens[b]) - (r1 - r0)
+            rows = [r for r in range(r0, r1) if wanted is None or r in wanted]
+            for i0 in range(0, len(rows), q_block):
+                blk = rows[i0:i0 + q_block]
+                pos = [(i0 + j if subset_index else r - r0) + (shift_later_blocks if i0 else 0)
+                       for j, r in enumerate(blk)]
+                for r, i in zip(blk, pos):
+                    lo, hi = A.prefill_attended_range(P + i, window)
+                    hi = min(hi, int(seq_lens[b]))
+                    keys = A.gather_positions(k_pool, block_tables[b], range(lo, hi), block_size)
+                    vals = A.gather_positions(v_pool, block_tables[b], range(lo, hi), block_size)
+                    for h in range(Hq):
+                        out[r, h] = A.attend_one(q[r, h], keys[:, h // group], vals[:, h // group], scale)
+        return out
+    return f
+
+
+MUTANTS["prefill later query blocks shifted by one row"] = ("prefill_chunk", _prefill_variant(shift_later_blocks=-1))
+MUTANTS["prefill query_rows position from the subset index"] = ("prefill_chunk", _prefill_variant(subset_index=True))
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
