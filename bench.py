@@ -303,6 +303,8 @@ def main():
     ap.add_argument("--waves", type=int, default=None, help="independent batches rotated through")
     ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"], help="KV pool element type")
     ap.add_argument("--head-dim", type=int, default=None, help="head_dim override (e.g. 512 for the hybrid decode)")
+    ap.add_argument("--partition-tokens", type=int, default=None,
+                    help="decode split-K partition size (default: the workload's, else the library rule)")
     ap.add_argument("--scrub", action="store_true",
                     help="read a 1 GiB buffer before every attention launch of the per-kernel timing pass, "
                          "so the roofline is taken with cold caches")
@@ -338,6 +340,8 @@ def main():
     fp8 = args.kv == "fp8"
     if args.head_dim:
         kw["head_dim"] = args.head_dim
+    if args.partition_tokens is not None:
+        kw["part"] = args.partition_tokens
     log(f"[bench] building workload {args.workload} ({kw})")
     wl = synth.make(args.workload, **kw)
     R = waves if args.workload == "qwen3" else 1

@@ -548,8 +548,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_lds_kernel(D
       for (int i = 0; i < NI; ++i) {
         // With block size 8, rows 8..15 are in the second block.
         const size_t base = (bs8 && i * TPI >= 8) ? base_hi : base_lo;
-        lds_dma16(kpool + base, voff[i], sl + i * 1024);
-        lds_dma16(vpool + base, voff[i], sl + SBYTES + i * 1024);
+        lds_dma16_stream(kpool + base, voff[i], sl + i * 1024);
+        lds_dma16_stream(vpool + base, voff[i], sl + SBYTES + i * 1024);
       }
     } else {
 #pragma unroll
@@ -560,8 +560,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_lds_kernel(D
         const size_t off = base + voff[i];
         const void* ksrc = ok ? static_cast<const void*>(kpool + off) : &kZeroChunk;
         const void* vsrc = ok ? static_cast<const void*>(vpool + off) : &kZeroChunk;
-        lds_dma16(ksrc, sl + i * 1024);
-        lds_dma16(vsrc, sl + SBYTES + i * 1024);
+        lds_dma16_stream(ksrc, sl + i * 1024);
+        lds_dma16_stream(vsrc, sl + SBYTES + i * 1024);
       }
     }
     return vmask;

@@ -119,6 +119,19 @@ __device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, uint3
                :: "s"(m0), "v"(voff), "s"(base) : "memory", "m0");
 }
 
+// Streaming forms (the nt cache policy: lines marked for early eviction), for
+// data a kernel reads exactly once, such as the decode kernels' K/V stages. A
+// plain read stream of a 2 GiB buffer, contiguous or in random 8 KiB chunks,
+// measured about 6.9 TB/s with the policy and 6.1-6.3 TB/s without.
+__device__ __forceinline__ void lds_dma16_stream(const void* gaddr, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
+               :: "s"(m0), "v"(gaddr) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma16_stream(const void* base, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+               :: "s"(m0), "v"(voff), "s"(base) : "memory", "m0");
+}
+
 // LDS byte offset of a __shared__ location: the low half of its generic
 // address (the high half is the LDS aperture).
 __device__ __forceinline__ uint32_t lds_offset(const void* p) {
