@@ -87,11 +87,13 @@ _SIGNATURES = {
     "paged_alloc_destroy": [_c_void_p],
     "paged_alloc_grow": [_c_void_p, _c_int32, _P_I32],
     "paged_alloc_num_blocks": [_c_void_p, _P_I32],
+    "paged_alloc_set_max_blocks": [_c_void_p, _c_int32],
     "paged_alloc_num_free": [_c_void_p, _P_I32, _P_I32],
     "paged_seq_add": [_c_void_p, _c_int64],
     "paged_seq_match_prefix": [_c_void_p, _c_int64, _P_I32, _c_int32, _c_uint64, _P_I32],
     "paged_seq_share_prefix": [_c_void_p, _c_int64, _c_int64, _c_int32],
     "paged_seq_reserve": [_c_void_p, _c_int64, _c_int32],
+    "paged_seq_reserve_or_grow": [_c_void_p, _c_int64, _c_int32, _P_I32],
     "paged_seq_commit_tokens": [_c_void_p, _c_int64, _P_I32, _c_int32],
     "paged_seq_publish_full_blocks": [_c_void_p, _c_int64, _c_uint64],
     "paged_seq_drop_outside_window": [_c_void_p, _c_int64, _c_int32],
@@ -463,6 +465,16 @@ class Allocator:
     def grow(self, new_num_blocks, new_order=None):
         keep, ptr = (None, None) if new_order is None else _i32_array(new_order)
         _check(lib.paged_alloc_grow(self._h, int(new_num_blocks), ptr))
+
+    def set_max_blocks(self, max_blocks):
+        _check(lib.paged_alloc_set_max_blocks(self._h, int(max_blocks)))
+
+    def reserve_or_grow(self, seq_id, total_tokens):
+        """0 when reserved; else the block count the pools must grow to first
+        (grow, then retry with ``reserve``)."""
+        out = ctypes.c_int32()
+        _check(lib.paged_seq_reserve_or_grow(self._h, int(seq_id), int(total_tokens), ctypes.byref(out)))
+        return out.value
 
     def num_free(self):
         f, e = ctypes.c_int32(), ctypes.c_int32()

@@ -66,6 +66,7 @@ struct Seq {
 struct paged_alloc {
   int32_t nb = 0;
   int32_t bs = 0;
+  int32_t max_nb = 0;  // grow-on-demand ceiling; the size at creation unless raised
   std::deque<int32_t> free_list;
   // Intrusive LRU of evictable published blocks (oldest at head).
   std::vector<int32_t> lru_prev, lru_next;
@@ -164,6 +165,7 @@ int32_t paged_alloc_create(int32_t num_blocks, int32_t block_size, const int32_t
       return fail(PAGED_ERR_INVALID_ARG, "free_order is not a permutation of 1..%d", num_blocks - 1);
     auto* a = new paged_alloc();
     a->nb = num_blocks;
+    a->max_nb = num_blocks;
     a->bs = block_size;
     a->resize_block_arrays(num_blocks);
     for (int32_t i = 0; i < num_blocks - 1; ++i)
@@ -190,8 +192,17 @@ int32_t paged_alloc_grow(paged_alloc* a, int32_t new_num_blocks, const int32_t* 
     a->resize_block_arrays(new_num_blocks);
     for (int32_t i = 0; i < added; ++i) a->free_list.push_back(new_order ? new_order[i] : a->nb + i);
     a->nb = new_num_blocks;
+    a->max_nb = std::max(a->max_nb, new_num_blocks);
     return ok();
   });
+}
+
+int32_t paged_alloc_set_max_blocks(paged_alloc* a, int32_t max_blocks) {
+  if (!a) return fail(PAGED_ERR_INVALID_ARG, "allocator is NULL");
+  if (max_blocks < a->nb)
+    return fail(PAGED_ERR_INVALID_ARG, "max_blocks %d is below the pool's %d blocks", max_blocks, a->nb);
+  a->max_nb = max_blocks;
+  return ok();
 }
 
 int32_t paged_alloc_num_blocks(const paged_alloc* a, int32_t* num_blocks) {
@@ -277,6 +288,28 @@ int32_t paged_seq_reserve(paged_alloc* a, int64_t seq_id, int32_t total_tokens) 
                   a->free_list.size(), a->lru_size);
     s->blocks.reserve(static_cast<size_t>(want));
     for (int64_t i = 0; i < need; ++i) s->blocks.push_back(a->take_new());
+    return ok();
+  });
+}
+
+int32_t paged_seq_reserve_or_grow(paged_alloc* a, int64_t seq_id, int32_t total_tokens,
+                                  int32_t* grow_to) {
+  PAGEDKV_GUARD([&]() -> int32_t {
+    if (!a || !grow_to) return fail(PAGED_ERR_INVALID_ARG, "NULL argument");
+    *grow_to = 0;
+    if (total_tokens < 0) return fail(PAGED_ERR_INVALID_ARG, "negative token count");
+    Seq* s = a->find(seq_id);
+    if (!s) return fail(PAGED_ERR_STATE, "unknown sequence %lld", (long long)seq_id);
+    const int64_t needed = (static_cast<int64_t>(total_tokens) + a->bs - 1) / a->bs -
+                           static_cast<int64_t>(s->blocks.size());
+    const int64_t avail = static_cast<int64_t>(a->free_list.size()) + a->lru_size;
+    // Fits in free + evictable blocks (or needs nothing): an ordinary reservation.
+    if (needed <= avail) return paged_seq_reserve(a, seq_id, total_tokens);
+    if (a->nb >= a->max_nb)
+      return fail(PAGED_ERR_NO_BLOCKS, "need %lld blocks, %lld free + evictable, pool at its maximum of %d",
+                  (long long)needed, (long long)avail, a->max_nb);
+    const int64_t target = std::max<int64_t>(2LL * a->nb, a->nb + needed);
+    *grow_to = static_cast<int32_t>(std::min<int64_t>(a->max_nb, target));
     return ok();
   });
 }

@@ -328,6 +328,11 @@ int32_t paged_alloc_destroy(paged_alloc* a);
  * (NULL = ascending); the caller grows its device pools to match first
  * (paged-cache doc, pool-sizing section: grow before evicting). */
 int32_t paged_alloc_grow(paged_alloc* a, int32_t new_num_blocks, const int32_t* new_order);
+/* Ceiling for paged_seq_reserve_or_grow (paged-cache doc, pool-sizing section:
+ * the maximum pool size). The default is the pool's size at creation (a fixed
+ * pool, which never asks to grow); paged_alloc_grow raises it to the new size
+ * when that is larger. PAGED_ERR_INVALID_ARG below the current block count. */
+int32_t paged_alloc_set_max_blocks(paged_alloc* a, int32_t max_blocks);
 int32_t paged_alloc_num_blocks(const paged_alloc* a, int32_t* num_blocks);
 int32_t paged_alloc_num_free(const paged_alloc* a, int32_t* free_blocks,
                              int32_t* evictable_blocks);
@@ -347,6 +352,19 @@ int32_t paged_seq_share_prefix(paged_alloc* a, int64_t dst_seq, int64_t src_seq,
 /* allocate_suffix_blocks: grow the table to ceil(total_tokens / block_size)
  * entries. PAGED_ERR_NO_BLOCKS (nothing changed) if free + evictable is short. */
 int32_t paged_seq_reserve(paged_alloc* a, int64_t seq_id, int32_t total_tokens);
+/* allocate_suffix_blocks with grow-on-demand (paged-cache doc, pool-sizing
+ * section: a reservation that outruns free + evictable blocks grows the pool
+ * before evicting; one grow, then one retry). With needed = the new blocks the
+ * reservation takes and cur = the pool's block count:
+ *   - needed <= free + evictable: reserved as by paged_seq_reserve
+ *     (free blocks first, then LRU eviction); *grow_to = 0;
+ *   - else, cur < max: nothing changes and *grow_to =
+ *     min(max, max(2 * cur, cur + needed)); the caller grows its device pools
+ *     to *grow_to blocks, calls paged_alloc_grow, then retries once with
+ *     paged_seq_reserve (which reserves, evicting as needed, or fails);
+ *   - else PAGED_ERR_NO_BLOCKS (nothing changed). */
+int32_t paged_seq_reserve_or_grow(paged_alloc* a, int64_t seq_id, int32_t total_tokens,
+                                  int32_t* grow_to);
 /* record_tokens: append n token ids (positions must already be reserved,
  * else PAGED_ERR_CAPACITY). */
 int32_t paged_seq_commit_tokens(paged_alloc* a, int64_t seq_id, const int32_t* tokens,

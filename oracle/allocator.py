@@ -34,6 +34,13 @@ The written policy (our reading where the pages leave details open):
 * Release walks the row's table from the last entry to the first (deepest
   first, so chain tails reach the LRU queue before their parents), skipping
   null entries.
+* Grow-on-demand (pool-sizing section): the pool has a maximum block count,
+  by default its size at creation (a fixed pool). A reservation that needs
+  more blocks than free + evictable hold asks for growth first, to
+  ``min(max, max(2 * current, current + needed))`` blocks, where ``needed`` is
+  the number of new blocks the reservation takes; the caller grows its pools
+  and retries the reservation once, which then allocates (free blocks first,
+  then LRU eviction) or fails. A pool already at its maximum fails at once.
 """
 
 from __future__ import annotations
@@ -85,6 +92,7 @@ class RefAllocator:
         self.table = {}                   # key -> block
         self.next_chain_id = 1
         self.seqs = {}
+        self.max_nb = self.nb             # grow-on-demand ceiling; a fixed pool by default
 
     # -- helpers ---------------------------------------------------------
     def _seq(self, seq_id):
@@ -130,6 +138,35 @@ class RefAllocator:
         self.key_of += [None] * grow_by
         self.free.extend(added)
         self.nb = new_num_blocks
+        self.max_nb = max(self.max_nb, self.nb)
+
+    def set_max_blocks(self, max_blocks):
+        """Ceiling of grow-on-demand (the pool-sizing section's maximum pool
+        size); at least the current block count."""
+        if int(max_blocks) < self.nb:
+            raise AllocError(ERR_INVALID_ARG, "max_blocks below the current pool size")
+        self.max_nb = int(max_blocks)
+
+    def reserve_or_grow(self, seq_id, total_tokens):
+        """allocate_suffix_blocks with grow-on-demand (mlx-node paged-cache doc,
+        pool-sizing section: a reservation that outruns free + evictable
+        blocks grows the pool before evicting, to min(max, max(2 x current,
+        current + needed)) blocks; one grow, then one retry).
+
+        Returns 0 when the reservation was made here. Otherwise nothing has
+        changed and the return value is the block count the pool must grow to;
+        the caller grows its pools, calls ``grow`` and retries with
+        ``reserve``. A pool at its maximum raises ERR_NO_BLOCKS."""
+        s = self._seq(seq_id)
+        if total_tokens < 0:
+            raise AllocError(ERR_INVALID_ARG, "negative token count")
+        needed = -(-int(total_tokens) // self.bs) - len(s.blocks)
+        if needed <= 0 or len(self.free) + len(self.lru) >= needed:
+            self.reserve(seq_id, total_tokens)
+            return 0
+        if self.nb >= self.max_nb:
+            raise AllocError(ERR_NO_BLOCKS, f"need {needed} blocks and the pool is at its maximum")
+        return min(self.max_nb, max(2 * self.nb, self.nb + needed))
 
     def add(self, seq_id):
         if int(seq_id) in self.seqs:

@@ -16,13 +16,18 @@ import block_paged_kv_amd as pk
 import synth
 from oracle import RefAllocator
 
-from test_ref_allocator import apply, check_invariants, random_script, run_script
+from test_ref_allocator import GROW_SCRIPTS, apply, check_invariants, random_script, run_script
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def test_golden_script_cpp():
     run_script(pk.Allocator, None)
+
+
+@pytest.mark.parametrize("idx", range(len(GROW_SCRIPTS)), ids=[s["name"] for s in GROW_SCRIPTS])
+def test_golden_grow_script_cpp(idx):
+    run_script(pk.Allocator, None, GROW_SCRIPTS[idx])
 
 
 def _snapshot(a, nb, ids):

@@ -19,14 +19,19 @@ from oracle import RefAllocator, AllocError
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
-def run_script(make, steps):
-    """Run the golden script on an allocator built by ``make(nb, bs, order)``.
+def load_golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def run_script(make, steps, script=None):
+    """Run a golden script (default: allocator_script.json) on an allocator
+    built by ``make(nb, bs, order)``.
 
     The allocator must offer the RefAllocator method names; failures must
     raise an exception with a ``.code`` attribute.
     """
-    with open(os.path.join(GOLDEN, "allocator_script.json")) as f:
-        g = json.load(f)
+    g = script if script is not None else load_golden("allocator_script.json")
     a = make(g["num_blocks"], g["block_size"], g["free_order"])
     for i, st in enumerate(g["steps"][:steps] if steps else g["steps"]):
         op, where = st["op"], f"step {i}: {st}"
@@ -66,6 +71,22 @@ def run_script(make, steps):
             a.release(st["seq"])
         elif op == "drop":
             a.drop_outside_window(st["seq"], st["window"])
+        elif op == "grow":
+            a.grow(st["blocks"], st["order"])
+        elif op == "set_max":
+            a.set_max_blocks(st["blocks"])
+        elif op == "set_max_fail":
+            with pytest.raises(Exception) as ei:
+                a.set_max_blocks(st["blocks"])
+            assert ei.value.code == st["code"], where
+        elif op == "reserve_or_grow":
+            assert a.reserve_or_grow(st["seq"], st["tokens"]) == st["expect_grow"], where
+        elif op == "reserve_or_grow_fail":
+            before = (a.num_free(), [list(map(int, r)) for r in a.block_tables([st["seq"]], 64)])
+            with pytest.raises(Exception) as ei:
+                a.reserve_or_grow(st["seq"], st["tokens"])
+            assert ei.value.code == st["code"], where
+            assert (a.num_free(), [list(map(int, r)) for r in a.block_tables([st["seq"]], 64)]) == before, where
         else:
             raise AssertionError(f"unknown op {op}")
     return a
@@ -73,6 +94,64 @@ def run_script(make, steps):
 
 def test_golden_script():
     run_script(RefAllocator, None)
+
+
+GROW_SCRIPTS = load_golden("allocator_grow_script.json")["scripts"]
+
+
+@pytest.mark.parametrize("idx", range(len(GROW_SCRIPTS)), ids=[s["name"] for s in GROW_SCRIPTS])
+def test_golden_grow_script(idx):
+    a = run_script(RefAllocator, None, GROW_SCRIPTS[idx])
+    check_invariants(a)
+
+
+def _grow_ignoring_order(self, new_num_blocks, new_order=None):
+    return _orig_grow(self, new_num_blocks, None)
+
+
+def _grow_prepending(self, new_num_blocks, new_order=None):
+    old = list(self.free)
+    _orig_grow(self, new_num_blocks, new_order)
+    added = list(self.free)[len(old):]
+    self.free.clear()
+    self.free.extend(added + old)
+
+
+def _reserve_or_grow_doubling_only(self, seq_id, total_tokens):
+    r = _orig_rog(self, seq_id, total_tokens)
+    return min(self.max_nb, 2 * self.nb) if r else r
+
+
+def _reserve_or_grow_on_free_only(self, seq_id, total_tokens):
+    """Grows whenever the free list alone is short (before any eviction)."""
+    s = self._seq(seq_id)
+    needed = -(-int(total_tokens) // self.bs) - len(s.blocks)
+    if needed > len(self.free) and self.nb < self.max_nb:
+        return min(self.max_nb, max(2 * self.nb, self.nb + needed))
+    return _orig_rog(self, seq_id, total_tokens)
+
+
+_orig_grow = RefAllocator.grow
+_orig_rog = RefAllocator.reserve_or_grow
+GROW_MUTANTS = {
+    "grow ignores the given order": ("grow", _grow_ignoring_order),
+    "grow puts new blocks at the free head": ("grow", _grow_prepending),
+    "grow-on-demand only doubles": ("reserve_or_grow", _reserve_or_grow_doubling_only),
+    "grow-on-demand when the free list alone is short": ("reserve_or_grow", _reserve_or_grow_on_free_only),
+}
+
+
+@pytest.mark.parametrize("name", sorted(GROW_MUTANTS))
+def test_grow_mutants_are_caught(name, monkeypatch):
+    attr, fn = GROW_MUTANTS[name]
+    monkeypatch.setattr(RefAllocator, attr, fn)
+    failures = 0
+    for sc in GROW_SCRIPTS:
+        try:
+            run_script(RefAllocator, None, sc)
+        except (Exception, pytest.fail.Exception):
+            failures += 1
+    assert failures > 0, f"no grow script catches the mutant '{name}'"
 
 
 def check_invariants(a: RefAllocator):
