@@ -69,7 +69,7 @@ __global__ __launch_bounds__(kThreads) void kv_write_kernel(
     const uint4 kv = new_k[i];
     const uint4 vv = new_v[i];
     const int64_t slot = slots[t];
-    if (slot < 0 || slot >= num_slots) continue;
+    if ((slot >> bs_log2) <= 0 || slot >= num_slots) continue;  // padding, the null block, out of range
     const int32_t h = r / vecs_per_head;
     const int32_t v = r - h * vecs_per_head;
     const int64_t blk = slot >> bs_log2;
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(kThreads) void kv_write_fp8_kernel(
     load16(new_k + i * 16, xk);
     load16(new_v + i * 16, xv);
     const int64_t slot = slots[t];
-    if (slot < 0 || slot >= num_slots) continue;
+    if ((slot >> bs_log2) <= 0 || slot >= num_slots) continue;  // padding, the null block, out of range
     const int32_t h = r / vecs_per_head;
     const int32_t v = r - h * vecs_per_head;
     const int64_t blk = slot >> bs_log2;

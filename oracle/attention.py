@@ -40,6 +40,10 @@ def kv_write(k_pool, v_pool, new_k, new_v, slot_mapping, block_size):
     slot its request owns. For token t with ``slot = slot_mapping[t] >= 0``:
     ``pool[slot // BS, :, slot % BS, :] = new[t]``. Tokens with a negative slot
     are padding and write nothing; every other pool element keeps its bits.
+    Block 0 is the shared null sentinel that sliding tables point at for
+    expired blocks (mlx-node paged-cache doc, hybrid coordinator paragraph);
+    no request owns a slot in it, so a slot there is read as padding too
+    (our reading: the pages never write the sentinel).
 
     The copy is element for element (numpy assignment of equal dtypes), so the
     result is bit-exact. Returns ``(k_pool', v_pool')``.
@@ -52,6 +56,8 @@ def kv_write(k_pool, v_pool, new_k, new_v, slot_mapping, block_size):
         if s < 0:
             continue
         blk, off = divmod(s, block_size)
+        if blk == 0:
+            continue
         k_out[blk, :, off, :] = new_k[t]
         v_out[blk, :, off, :] = new_v[t]
     return k_out, v_out

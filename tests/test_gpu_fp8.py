@@ -60,7 +60,7 @@ def test_fp8_quantizer_rounding_and_saturation(pk, src):
 
     announce(f"fp8 quantizer {src}")
     rng = np.random.default_rng(11)
-    T, H, D, NB, BS = 48, 2, 128, 4, 16
+    T, H, D, NB, BS = 48, 2, 128, 5, 16
     x = rng.standard_normal((T, H, D)) * 10.0 ** rng.uniform(-5, 3, size=(T, H, D))
     ties = np.array([1.0625, 1.1875, 432.0, 464.0, 500.0, 1e4, 2.0 ** -10, 1.5 * 2.0 ** -9,
                      0.5 * 2.0 ** -9, 3 * 2.0 ** -10], dtype=np.float64)
@@ -69,7 +69,7 @@ def test_fp8_quantizer_rounding_and_saturation(pk, src):
     dt = torch.bfloat16 if src == "bf16" else torch.float32
     xt = torch.from_numpy(x.astype(np.float32)).to(dtype=dt, device="cuda")
     xs = xt.float().cpu().numpy()  # the exact source values (bf16-rounded for bf16)
-    slots = torch.arange(T, dtype=torch.int64, device="cuda") * 1 + 3
+    slots = torch.arange(T, dtype=torch.int64, device="cuda") + BS + 3  # block 1 onwards
     for k_scale, v_scale in ((1.0, 1.0), (0.0123, 7.5)):
         kp = torch.full((NB, H, BS, D), float("nan"), dtype=torch.float8_e4m3fn, device="cuda")
         vp = torch.full_like(kp, float("nan"))

@@ -221,6 +221,20 @@ def pin_write_then_gather_roundtrip():
     assert np.all(~np.isnan(k2t[touched])) and np.all(~np.isnan(v2t[touched]))
 
 
+def pin_write_skips_the_null_block():
+    """A slot inside block 0 (the shared null sentinel) writes nothing; the
+    other tokens of the same call are written."""
+    nb, hkv, bs, d = 4, 1, 4, 2
+    kp = np.full((nb, hkv, bs, d), np.nan, dtype=np.float32)
+    vp = kp.copy()
+    new = np.arange(3 * hkv * d, dtype=np.float32).reshape(3, hkv, d)
+    k2, v2 = oracle.kv_write(kp, vp, new, new + 100, [2, 9, 3], bs)   # slots 2, 3 lie in block 0
+    assert np.all(np.isnan(k2[0])) and np.all(np.isnan(v2[0]))
+    np.testing.assert_array_equal(k2[2, :, 1], new[1])
+    np.testing.assert_array_equal(v2[2, :, 1], new[1] + 100)
+    assert np.isnan(k2).sum() == k2.size - hkv * d
+
+
 def pin_null_block_never_read():
     rng = np.random.default_rng(15)
     nb, hkv, bs, d = 8, 1, 4, 2
