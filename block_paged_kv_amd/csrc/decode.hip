@@ -10,22 +10,24 @@
 // How (ours): the row's span, starting at the first live block, is cut into
 // partitions of `part` positions (perf doc, attention-partitions paragraph:
 // partitioned decode with a separate reducer; empty partitions add nothing).
-// One workgroup of up to four 64-lane waves handles (row, KV head, group of
-// GT query heads, partition). Memory mapping:
-//   * a token row of K (head_dim elements, 128..512 bytes) is read by R = 16
-//     (or 8) consecutive lanes with 16-byte loads, so one wave instruction
-//     reads 64/R consecutive token rows = 1 KiB of one contiguous block slab;
-//   * each iteration a lane issues 16 K loads and 16 V loads back to back
-//     (32 KiB per wave in flight) before touching any of them;
-//   * q.k is v_dot2_f32_bf16 (two bf16 products per instruction) followed by a
-//     DPP sum over the R lanes of the row; the score is then known to every
-//     lane of the row, so the online softmax runs per "token lane" with no
-//     cross-row traffic, and P.V accumulates in fp32 in the lane that owns
-//     those head_dim elements;
-//   * the token lanes of a wave, then the waves of a workgroup (through LDS),
-//     are merged once at the end. Partials are fp32 (max in log2 units, sum,
-//     unnormalised accumulator); the reduce kernel combines them in partition
-//     order, so results are deterministic and there are no atomics.
+// One workgroup handles (row, KV head, group of GT query heads, partition) and
+// writes float32 partials (max in log2 units, sum, unnormalised accumulator);
+// decode_reduce_kernel combines a row's partitions in partition order, so
+// results are deterministic and there are no atomics. When every row fits one
+// partition the partial kernel writes the output itself and no reduce runs.
+//   * bf16 and FP8 pools (decode_partial_lds_kernel): four waves, each
+//     streaming its share of the partition's 16-token K/V stages from the
+//     pages straight into a private LDS ring with global_load_lds_dwordx4
+//     (streaming cache policy), two stages in flight; S^T = K Q^T and
+//     O += P V on the matrix cores; the waves merge through LDS at the end.
+//     See the comment above that kernel for the layout.
+//   * fp32 pools (decode_partial_kernel): up to four waves on the vector ALU.
+//     A token row of K is read by R = 16 (or 8) consecutive lanes with
+//     16-byte loads, 16 K and 16 V loads per lane in flight before any is
+//     used; q.k is an fp32 FMA chain followed by a DPP sum over the R lanes,
+//     so every lane of a row knows the score and the online softmax runs per
+//     "token lane"; P.V accumulates in the lane owning those head_dim
+//     elements; token lanes, then waves (through LDS), merge at the end.
 
 #include <cmath>
 
@@ -826,111 +828,95 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_lds_kernel(D
 }
 
 
-// One wave per (row, query head): combine that pair's partitions in order.
-// The row length, the first 64 partitions' (max, sum) and the first 16
-// partitions' accumulators are requested together, before the row's
-// partition count is known (entries past it are fetched but never used), so
-// a typical call needs one round trip to memory before the store. More
-// partitions are summed with eight loads in flight at a time.
-template <int ESZ, int D>
+// Combine each (row, query head) pair's partitions. WPP waves serve one pair
+// (a 256-thread workgroup serves 4 / WPP pairs); lane l of the pair's wave w
+// owns head_dim columns 64 w + l + 64 WPP k, k < CPT = D / (64 WPP).
+// Partitions are taken in chunks of CH = 64 / CPT (at most 64): lane i of
+// every wave holds the chunk's partition i (max, sum). The launcher picks the
+// fewest waves per pair for which a row's partitions fit one chunk, so that
+// the row length, the (max, sum) pairs and every accumulator are requested
+// together, before the row's live partition count is known (entries past it
+// are fetched but never used, only selected away): one round trip to memory
+// before the store. Longer rows take further chunks, combined in order with
+// an online maximum; the result does not depend on how many empty partitions
+// follow the live ones.
+template <int ESZ, int D, int CPT>
 __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeParams a) {
   constexpr float kNegInf = -INFINITY;
-  constexpr int PER_LANE = D / 64;
-  constexpr int PF = 16;
-  const int wave = threadIdx.x >> 6;
-  const int pair = blockIdx.x * 4 + wave;
-  if (pair >= a.batch * a.hq) return;
+  constexpr int WPP = D / (64 * CPT);          // waves per pair
+  constexpr int CH = 64 / CPT;                 // partitions per chunk
+  static_assert(WPP >= 1 && WPP <= 4 && D == 64 * CPT * WPP, "bad reduce shape");
   const int lane = threadIdx.x & 63;
-  const int b = pair / a.hq;
+  const int wave = threadIdx.x >> 6;
+  const int b = blockIdx.y;
+  const int h = blockIdx.x * (4 / WPP) + wave / WPP;
+  if (h >= a.hq) return;
+  const int pair = b * a.hq + h;
+  const int c0l = (wave % WPP) * 64 + lane;    // first column of this lane
   const int P = a.max_parts;
   const float* ml = a.ws_ml + static_cast<size_t>(pair) * P * 2;
   const float* acc = a.ws_acc + static_cast<size_t>(pair) * P * D;
 
   const int n = a.seq_lens[b];
-  const float mp0 = lane < P ? ml[2 * lane] : kNegInf;
-  const float lp0 = lane < P ? ml[2 * lane + 1] : 0.f;
-  float xf[PF][PER_LANE];
+  // First chunk, requested before anything is waited for.
+  float2 mlc = lane < CH && lane < P ? *reinterpret_cast<const float2*>(ml + 2 * lane) : make_float2(kNegInf, 0.f);
+  float x[CH][CPT];
 #pragma unroll
-  for (int q = 0; q < PF; ++q)
+  for (int u = 0; u < CH; ++u)
 #pragma unroll
-    for (int k = 0; k < PER_LANE; ++k)
-      xf[q][k] = q < P ? acc[static_cast<size_t>(q) * D + lane + 64 * k] : 0.f;
+    for (int k = 0; k < CPT; ++k)
+      x[u][k] = u < P ? acc[static_cast<size_t>(u) * D + c0l + 64 * WPP * k] : 0.f;
 
   const int lo = a.window > 0 ? max(0, n - a.window) : 0;
   const int s0 = (lo >> a.bs_log2) << a.bs_log2;
   const int np = n > s0 ? min((n - s0 + a.part - 1) / a.part, P) : 0;
-  float o[PER_LANE];
+
+  float o[CPT];
 #pragma unroll
-  for (int k = 0; k < PER_LANE; ++k) o[k] = 0.f;
-  float L = 0.f;
-  float Mprev = kNegInf;
-  for (int p0 = 0; p0 < np; p0 += 64) {
-    // (max, sum) of partitions p0 + lane; the running max M covers all chunks.
-    const int p = p0 + lane;
-    float mp, lp;
-    if (p0 == 0) {
-      mp = p < np ? mp0 : kNegInf;
-      lp = p < np ? lp0 : 0.f;
-    } else {
-      mp = p < np ? ml[2 * p] : kNegInf;
-      lp = p < np ? ml[2 * p + 1] : 0.f;
+  for (int k = 0; k < CPT; ++k) o[k] = 0.f;
+  float M = kNegInf, L = 0.f;
+  for (int c0 = 0; c0 < np; c0 += CH) {
+    if (c0 > 0) {
+      // Later chunks (rows with more than CH partitions).
+      const int pl = c0 + lane;
+      mlc = lane < CH && pl < P ? *reinterpret_cast<const float2*>(ml + 2 * static_cast<size_t>(pl))
+                                : make_float2(kNegInf, 0.f);
+#pragma unroll
+      for (int u = 0; u < CH; ++u)
+#pragma unroll
+        for (int k = 0; k < CPT; ++k)
+          x[u][k] = c0 + u < P ? acc[static_cast<size_t>(c0 + u) * D + c0l + 64 * WPP * k] : 0.f;
     }
-    float M = mp;
+    const bool live = lane < CH && c0 + lane < np;
+    const float mp = live ? mlc.x : kNegInf;
+    const float lp = live ? mlc.y : 0.f;
+    float cm = mp;
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    // Chunks beyond the first (more than 64 partitions) rescale what came before.
-    if (p0 > 0) {
-      const float newM = fmaxf(Mprev, M);
-      const float f = Mprev == kNegInf ? 0.f : fast_exp2(Mprev - newM);
-      L *= f;
-#pragma unroll
-      for (int k = 0; k < PER_LANE; ++k) o[k] *= f;
-      M = newM;
-    }
-    const float w = mp == kNegInf ? 0.f : fast_exp2(mp - M);
+    for (int off = 32; off > 0; off >>= 1) cm = fmaxf(cm, __shfl_xor(cm, off));
+    const float newM = fmaxf(M, cm);
+    // Earlier chunks' sums move to the new reference; empty partitions (max
+    // -inf) weigh exactly zero.
+    const float f = M == kNegInf ? 0.f : fast_exp2(M - newM);
+    const float w = mp == kNegInf ? 0.f : fast_exp2(mp - newM);
     float lw = lp * w;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) lw += __shfl_xor(lw, off);
-    L += lw;
-    const int cnt = min(64, np - p0);
-    int q = 0;
-    if (p0 == 0) {
+    L = L * f + lw;
 #pragma unroll
-      for (int qq = 0; qq < PF; ++qq) {
-        if (qq < cnt) {
-          const float wq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), qq));
+    for (int k = 0; k < CPT; ++k) o[k] *= f;
 #pragma unroll
-          for (int k = 0; k < PER_LANE; ++k) o[k] = fmaf(xf[qq][k], wq, o[k]);
-        }
-      }
-      q = min(cnt, PF);
+    for (int u = 0; u < CH; ++u) {
+      const float wu = __shfl(w, u);  // partition c0 + u, held by lane u
+      const bool take = c0 + u < np;
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) o[k] = fmaf(take ? x[u][k] : 0.f, wu, o[k]);
     }
-    for (; q + 8 <= cnt; q += 8) {
-      float x[8][PER_LANE];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int k = 0; k < PER_LANE; ++k)
-          x[i][k] = acc[static_cast<size_t>(p0 + q + i) * D + lane + 64 * k];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float wq = __shfl(w, q + i);
-#pragma unroll
-        for (int k = 0; k < PER_LANE; ++k) o[k] = fmaf(x[i][k], wq, o[k]);
-      }
-    }
-    for (; q < cnt; ++q) {
-      const float wq = __shfl(w, q);
-#pragma unroll
-      for (int k = 0; k < PER_LANE; ++k)
-        o[k] = fmaf(acc[static_cast<size_t>(p0 + q) * D + lane + 64 * k], wq, o[k]);
-    }
-    Mprev = M;
+    M = newM;
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
-  for (int k = 0; k < PER_LANE; ++k)
-    store_out<ESZ>(a.out, static_cast<size_t>(pair) * D + lane + 64 * k, o[k] * inv);
+  for (int k = 0; k < CPT; ++k)
+    store_out<ESZ>(a.out, static_cast<size_t>(pair) * D + c0l + 64 * WPP * k, o[k] * inv);
 }
 
 // Tokens one wave of the fp32 kernel processes per iteration.
@@ -1069,16 +1055,48 @@ void launch_partial_any(const DecodeParams& prm, int kv_esz, int d, int gt, dim3
   }
 }
 
+// Waves per (row, query head) for the reduce: the fewest for which the
+// pair's partitions (up to 64) fit one chunk of 64 / columns-per-lane.
+int reduce_waves_per_pair(int d, int max_parts) {
+  const int p = std::min(max_parts, 64);
+  for (int wpp = 1; wpp <= 4; wpp *= 2) {
+    const int cpt = d / (64 * wpp);
+    if (cpt >= 1 && cpt * p <= 64) return wpp;
+  }
+  return d >= 256 ? 4 : d / 64;
+}
+
+template <int ESZ, int D>
+void launch_reduce_w(const DecodeParams& prm, int wpp, hipStream_t s, const LaunchTrace& tr) {
+  const dim3 block(256);
+  auto go = [&](auto kern, int pairs_per_wg) {
+    const dim3 grid(static_cast<unsigned>((prm.hq + pairs_per_wg - 1) / pairs_per_wg),
+                    static_cast<unsigned>(prm.batch));
+    hipExtLaunchKernelGGL(kern, grid, block, 0, s, tr.start(), tr.stop(), 0, prm);
+  };
+  if constexpr (D == 64) {
+    go(decode_reduce_kernel<ESZ, 64, 1>, 4);
+  } else if constexpr (D == 128) {
+    if (wpp == 1) go(decode_reduce_kernel<ESZ, 128, 2>, 4);
+    else go(decode_reduce_kernel<ESZ, 128, 1>, 2);
+  } else if constexpr (D == 256) {
+    if (wpp == 1) go(decode_reduce_kernel<ESZ, 256, 4>, 4);
+    else if (wpp == 2) go(decode_reduce_kernel<ESZ, 256, 2>, 2);
+    else go(decode_reduce_kernel<ESZ, 256, 1>, 1);
+  } else {
+    if (wpp == 1) go(decode_reduce_kernel<ESZ, 512, 8>, 4);
+    else if (wpp == 2) go(decode_reduce_kernel<ESZ, 512, 4>, 2);
+    else go(decode_reduce_kernel<ESZ, 512, 2>, 1);
+  }
+}
+
 template <int ESZ>
-void launch_reduce_d(const DecodeParams& prm, int d, dim3 grid, hipStream_t s, const LaunchTrace& tr) {
-  if (d == 64)
-    hipExtLaunchKernelGGL(decode_reduce_kernel<ESZ, 64>, grid, dim3(256), 0, s, tr.start(), tr.stop(), 0, prm);
-  else if (d == 128)
-    hipExtLaunchKernelGGL(decode_reduce_kernel<ESZ, 128>, grid, dim3(256), 0, s, tr.start(), tr.stop(), 0, prm);
-  else if (d == 256)
-    hipExtLaunchKernelGGL(decode_reduce_kernel<ESZ, 256>, grid, dim3(256), 0, s, tr.start(), tr.stop(), 0, prm);
-  else if constexpr (ESZ == 2)
-    hipExtLaunchKernelGGL(decode_reduce_kernel<ESZ, 512>, grid, dim3(256), 0, s, tr.start(), tr.stop(), 0, prm);
+void launch_reduce_d(const DecodeParams& prm, int d, hipStream_t s, const LaunchTrace& tr) {
+  const int wpp = reduce_waves_per_pair(d, prm.max_parts);
+  if (d == 64) launch_reduce_w<ESZ, 64>(prm, wpp, s, tr);
+  else if (d == 128) launch_reduce_w<ESZ, 128>(prm, wpp, s, tr);
+  else if (d == 256) launch_reduce_w<ESZ, 256>(prm, wpp, s, tr);
+  else if constexpr (ESZ == 2) launch_reduce_w<ESZ, 512>(prm, wpp, s, tr);
 }
 
 }  // namespace
@@ -1121,6 +1139,61 @@ extern "C" int32_t paged_attn_decode_workspace_bytes(int32_t batch, int32_t num_
 
 namespace pagedkv {
 
+namespace {
+
+int32_t decode_check_plan(const void* out, const void* q, const void* k_pool, const void* v_pool,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                          int32_t num_blocks, float scale, float k_scale, float v_scale,
+                          int32_t sliding_window, int32_t partition_tokens, int32_t max_seq_len,
+                          const void* workspace, size_t workspace_bytes, int esz, Plan* pl) {
+  if (int32_t rc = make_plan(batch, num_q_heads, num_kv_heads, head_dim, block_size, max_seq_len,
+                             sliding_window, partition_tokens, esz, pl))
+    return rc;
+  if (max_blocks_per_seq < 1 || num_blocks < 1)
+    return fail(PAGED_ERR_INVALID_ARG, "max_blocks_per_seq and num_blocks must be positive");
+  if (!(std::isfinite(scale) && scale > 0.f))
+    return fail(PAGED_ERR_INVALID_ARG, "scale must be finite and positive");
+  if (!(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
+    return fail(PAGED_ERR_INVALID_ARG, "k_scale and v_scale must be finite and positive");
+  if (batch > 65535 || num_q_heads > 65535)
+    return fail(PAGED_ERR_INVALID_ARG, "batch and num_q_heads must be at most 65535");
+  if (pl->max_parts > 65535)
+    return fail(PAGED_ERR_INVALID_ARG,
+                "max_seq_len %d needs %d partitions of %d tokens; at most 65535 are supported",
+                max_seq_len, pl->max_parts, pl->part);
+  if (batch == 0) return ok();
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !seq_lens)
+    return fail(PAGED_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
+    return fail(PAGED_ERR_INVALID_ARG, "misaligned pointer");
+  if (!pl->direct) {
+    if (!workspace || !aligned16(workspace))
+      return fail(PAGED_ERR_INVALID_ARG, "workspace is NULL or misaligned");
+    if (workspace_bytes < pl->ws_bytes)
+      return fail(PAGED_ERR_CAPACITY, "workspace needs %zu bytes, got %zu", pl->ws_bytes,
+                  workspace_bytes);
+  }
+  return ok();
+}
+
+}  // namespace
+
+int32_t decode_check(const void* out, const void* q, const void* k_pool, const void* v_pool,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                     int32_t num_blocks, float scale, float k_scale, float v_scale,
+                     int32_t sliding_window, int32_t partition_tokens, int32_t max_seq_len,
+                     const void* workspace, size_t workspace_bytes, int esz) {
+  Plan pl;
+  return decode_check_plan(out, q, k_pool, v_pool, block_tables, max_blocks_per_seq, seq_lens,
+                           batch, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                           scale, k_scale, v_scale, sliding_window, partition_tokens, max_seq_len,
+                           workspace, workspace_bytes, esz, &pl);
+}
+
 // Shared by the bf16/fp32 and the FP8 entry points and the mixed step. esz:
 // pool element bytes (q/out are bf16 when esz == 1).
 int32_t decode_impl(void* out, const void* q, const void* k_pool, const void* v_pool,
@@ -1131,32 +1204,13 @@ int32_t decode_impl(void* out, const void* q, const void* k_pool, const void* v_
                     int32_t sliding_window, int32_t partition_tokens, int32_t max_seq_len,
                     void* workspace, size_t workspace_bytes, int esz, void* stream) {
   Plan pl;
-  if (int32_t rc = make_plan(batch, num_q_heads, num_kv_heads, head_dim, block_size, max_seq_len,
-                             sliding_window, partition_tokens, esz, &pl))
+  if (int32_t rc = decode_check_plan(out, q, k_pool, v_pool, block_tables, max_blocks_per_seq,
+                                     seq_lens, batch, num_q_heads, num_kv_heads, head_dim,
+                                     block_size, num_blocks, scale, k_scale, v_scale,
+                                     sliding_window, partition_tokens, max_seq_len, workspace,
+                                     workspace_bytes, esz, &pl))
     return rc;
-  if (max_blocks_per_seq < 1 || num_blocks < 1)
-    return fail(PAGED_ERR_INVALID_ARG, "max_blocks_per_seq and num_blocks must be positive");
-  if (!std::isfinite(scale)) return fail(PAGED_ERR_INVALID_ARG, "scale must be finite");
-  if (!(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
-    return fail(PAGED_ERR_INVALID_ARG, "k_scale and v_scale must be finite and positive");
-  if (batch > 65535 || num_q_heads > 65535)
-    return fail(PAGED_ERR_INVALID_ARG, "batch and num_q_heads must be at most 65535");
-  if (pl.max_parts > 65535)
-    return fail(PAGED_ERR_INVALID_ARG,
-                "max_seq_len %d needs %d partitions of %d tokens; at most 65535 are supported",
-                max_seq_len, pl.max_parts, pl.part);
   if (batch == 0) return ok();
-  if (!out || !q || !k_pool || !v_pool || !block_tables || !seq_lens)
-    return fail(PAGED_ERR_INVALID_ARG, "NULL pointer");
-  if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
-    return fail(PAGED_ERR_INVALID_ARG, "misaligned pointer");
-  if (!pl.direct) {
-    if (!workspace || !aligned16(workspace))
-      return fail(PAGED_ERR_INVALID_ARG, "workspace is NULL or misaligned");
-    if (workspace_bytes < pl.ws_bytes)
-      return fail(PAGED_ERR_CAPACITY, "workspace needs %zu bytes, got %zu", pl.ws_bytes,
-                  workspace_bytes);
-  }
   DecodeParams prm{};
   prm.out = pl.direct ? out : nullptr;
   prm.ws_acc = static_cast<float*>(workspace);
@@ -1198,10 +1252,9 @@ int32_t decode_impl(void* out, const void* q, const void* k_pool, const void* v_
   }
   if (!pl.direct) {
     prm.out = out;
-    const dim3 rgrid(static_cast<unsigned>((static_cast<int64_t>(batch) * num_q_heads + 3) / 4));
     LaunchTrace tr(PAGED_KERNEL_DECODE_REDUCE, s);
-    if (esz <= 2) launch_reduce_d<2>(prm, head_dim, rgrid, s, tr);  // bf16 output
-    else launch_reduce_d<4>(prm, head_dim, rgrid, s, tr);
+    if (esz <= 2) launch_reduce_d<2>(prm, head_dim, s, tr);  // bf16 output
+    else launch_reduce_d<4>(prm, head_dim, s, tr);
     tr.finish();
     if (int32_t rc = check_launch("paged_attn_decode (reduce)")) return rc;
   }

@@ -11,8 +11,6 @@
 // device instead of running one after the other; the caller's stream waits
 // for both before anything enqueued after the call.
 
-#include <cmath>
-
 #include "attn.h"
 #include "runtime.h"
 
@@ -49,31 +47,29 @@ extern "C" int32_t paged_attn_mixed(void* out, const void* q, const void* k_pool
                         seq_lens, np, total_q, max_q_len, num_q_heads, num_kv_heads, head_dim,
                         block_size, num_blocks, scale, k_scale, v_scale, sliding_window, esz, stream);
 
-  // Both parts: check what either could reject before enqueuing anything.
-  if (!out || !q || !k_pool || !v_pool || !block_tables || !cu_q_lens || !seq_lens)
-    return fail(PAGED_ERR_INVALID_ARG, "NULL pointer");
-  if (head_dim != 64 && head_dim != 128 && head_dim != 256 && head_dim != 512)
-    return fail(PAGED_ERR_INVALID_ARG, "head_dim must be 64, 128, 256 or 512 (got %d)", head_dim);
-  if (!std::isfinite(scale) || scale < 0.f)
-    return fail(PAGED_ERR_INVALID_ARG, "scale must be finite and non-negative");
-  if (!(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
-    return fail(PAGED_ERR_INVALID_ARG, "k_scale and v_scale must be finite and positive");
-  size_t need = 0;
-  if (int32_t rc = paged_attn_decode_workspace_bytes(nd, num_q_heads, num_kv_heads, head_dim, block_size,
-                                                     max_seq_len, sliding_window, partition_tokens,
-                                                     kv_dtype, &need))
+  // Both parts: check everything either could reject before enqueuing anything.
+  if (int32_t rc = prefill_check(out, q, k_pool, v_pool,
+                                 block_tables + static_cast<size_t>(nd) * max_blocks_per_seq,
+                                 max_blocks_per_seq, cu_q_lens + nd, seq_lens + nd, np, total_q - nd,
+                                 max_q_len, num_q_heads, num_kv_heads, head_dim, block_size,
+                                 num_blocks, scale, k_scale, v_scale, sliding_window))
     return rc;
-  if (need > 0 && (!workspace || workspace_bytes < need))
-    return fail(PAGED_ERR_CAPACITY, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+  if (int32_t rc = decode_check(out, q, k_pool, v_pool, block_tables, max_blocks_per_seq, seq_lens, nd,
+                                num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                                k_scale, v_scale, sliding_window, partition_tokens, max_seq_len,
+                                workspace, workspace_bytes, esz))
+    return rc;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   SideStream side(s);
   if (side.status() != PAGED_OK) return side.status();
   // Chunk rows first (the long kernel starts first), on the side stream: their
-  // cu_q_lens entries are absolute offsets into q and out. The prefill runs
-  // four-wave workgroups, two per CU: once one of them finishes, decode
-  // workgroups fit beside the other (an eight-wave workgroup would hold its
-  // CU's registers until the end).
+  // cu_q_lens entries are absolute offsets into q and out. Up to head_dim 128
+  // the prefill runs four-wave workgroups, two per CU: once one of them
+  // finishes, decode workgroups fit beside the other (an eight-wave workgroup
+  // would hold its CU's registers until the end). At head_dim 256 and 512 the
+  // prefill keeps its own shape (eight and four waves), whose tiles take most
+  // of a CU's LDS.
   int32_t rc = prefill_impl(out, q, k_pool, v_pool, block_tables + static_cast<size_t>(nd) * max_blocks_per_seq,
                             max_blocks_per_seq, cu_q_lens + nd, seq_lens + nd, np, total_q - nd,
                             max_q_len, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,

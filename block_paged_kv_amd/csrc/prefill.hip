@@ -217,8 +217,14 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
   uint2 kraw[ESZ == 1 ? KI : 1], vraw[ESZ == 1 ? KI : 1];  // FP8: codes awaiting their widening store
   const char* kpool = static_cast<const char*>(a.k_pool);
   const char* vpool = static_cast<const char*>(a.v_pool);
-  auto stage_load = [&](int kt, int ent, int buf) {
+  // Returns the tile's absent-block mask: bit i set when the tile's i-th
+  // block holds keys of the row (below n) but its table entry is not a valid
+  // block id (0, >= num_blocks, or a column past max_blocks_per_seq). Those
+  // keys are staged as zeros and masked out of the softmax, as in decode.
+  auto stage_load = [&](int kt, int ent, int buf) -> uint64_t {
     const int ts = kt * kTileN;
+    const int lb_tile = (ts >> bs_log2) + lane;
+    const uint64_t absent = __ballot(lane < tile_blocks && (lb_tile << bs_log2) < n && !phys_ok(ent));
     const int e0 = (wave * KPW) >> bs_log2;
     const int phys_lo = __builtin_amdgcn_readlane(ent, e0);
     const int phys_hi = __builtin_amdgcn_readlane(ent, split ? e0 + 1 : e0);
@@ -273,6 +279,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
         }
       }
     }
+    return absent;
   };
   // Completes the staging of buffer `buf` for this wave: the direct loads
   // have landed (bf16), or the widened registers are stored (FP8). A barrier
@@ -333,7 +340,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
   // ---- online softmax (lane: query 16j+lq, keys ts + 16*t4 + 4*lg + i) --------
   // Tiles that lie wholly inside every row's [lo, a] range skip the mask. The
   // probabilities are produced in 32-key steps, one P operand per step.
-  auto tile_softmax = [&](Scores& sc, bool need_mask, int ts) {
+  auto tile_softmax = [&](Scores& sc, bool need_mask, int ts, uint64_t absent) {
     if (need_mask) {
       // Rows past the tile's last row keep their (zero-query) scores: their
       // outputs are never stored. The empty asm makes the bounds opaque so
@@ -349,6 +356,19 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
           for (int i = 0; i < 4; ++i) {
             const int e = t4 * 16 + i;
             if (e < lo_rel || e > hi_rel) sc[j][t4][i] = kNegInf;
+          }
+      }
+      if (absent) {
+        // Keys of blocks with an invalid table entry are attended by nobody.
+        const int b0 = ts >> bs_log2;
+#pragma unroll
+        for (int t4 = 0; t4 < NS; ++t4)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = ts + t4 * 16 + 4 * lg + i;
+            if ((absent >> ((key >> bs_log2) - b0)) & 1u)
+#pragma unroll
+              for (int j = 0; j < JT; ++j) sc[j][t4][i] = kNegInf;
           }
       }
     }
@@ -486,7 +506,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
   auto needs_mask = [&](int ts) { return (ts + kTileN - 1 > a_min) || (ts < lo_max); };
 
   int ent_next = load_entries(kt_begin + 1);
-  stage_load(kt_begin, load_entries(kt_begin), 0);
+  uint64_t absent_next = stage_load(kt_begin, load_entries(kt_begin), 0);
   stage_store(0);
   __syncthreads();
 
@@ -498,15 +518,16 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
   for (int kt = kt_begin; kt <= kt_end; ++kt) {
     const int buf = (kt - kt_begin) & 1;
     const bool has_next = kt < kt_end;
+    const uint64_t absent = absent_next;
     if (has_next) {
-      stage_load(kt + 1, ent_next, buf ^ 1);
+      absent_next = stage_load(kt + 1, ent_next, buf ^ 1);
       ent_next = load_entries(kt + 2);
     }
     const int ts = kt * kTileN;
     __builtin_amdgcn_s_setprio(1);
     tile_s(sc, k_s[buf]);
     __builtin_amdgcn_s_setprio(0);
-    tile_softmax(sc, needs_mask(ts), ts);
+    tile_softmax(sc, needs_mask(ts) || absent != 0, ts, absent);
     // FP8 codes up to head_dim 128 are widened into the other buffer before
     // the P.V part, so the LDS stores drain under it rather than before the
     // barrier (their loads have landed by then; measured 5% faster, and no
@@ -548,13 +569,13 @@ namespace pagedkv {
 
 // Shared by the bf16 and FP8 entry points and the mixed step; esz: pool
 // element bytes (q/out bf16).
-int32_t prefill_impl(void* out, const void* q, const void* k_pool, const void* v_pool,
-                     const int32_t* block_tables, int32_t max_blocks_per_seq,
-                     const int32_t* cu_q_lens, const int32_t* seq_lens, int32_t batch,
-                     int32_t total_q, int32_t max_q_len, int32_t num_q_heads,
-                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                     int32_t num_blocks, float scale, float k_scale, float v_scale,
-                     int32_t sliding_window, int esz, void* stream, int waves) {
+int32_t prefill_check(const void* out, const void* q, const void* k_pool, const void* v_pool,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* cu_q_lens, const int32_t* seq_lens, int32_t batch,
+                      int32_t total_q, int32_t max_q_len, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                      int32_t num_blocks, float scale, float k_scale, float v_scale,
+                      int32_t sliding_window) {
   if (head_dim != 64 && head_dim != 128 && head_dim != 256 && head_dim != 512)
     return fail(PAGED_ERR_INVALID_ARG, "head_dim must be 64, 128, 256 or 512 (got %d)", head_dim);
   if (!pow2_in(block_size, 8, 64))
@@ -564,8 +585,8 @@ int32_t prefill_impl(void* out, const void* q, const void* k_pool, const void* v
   if (batch < 0 || total_q < 0 || max_q_len < 0 || max_blocks_per_seq < 1 || num_blocks < 1 ||
       sliding_window < 0)
     return fail(PAGED_ERR_INVALID_ARG, "bad size argument");
-  if (!std::isfinite(scale) || scale < 0.f)
-    return fail(PAGED_ERR_INVALID_ARG, "scale must be finite and non-negative");
+  if (!(std::isfinite(scale) && scale > 0.f))
+    return fail(PAGED_ERR_INVALID_ARG, "scale must be finite and positive");
   if (!(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
     return fail(PAGED_ERR_INVALID_ARG, "k_scale and v_scale must be finite and positive");
   if (batch == 0 || total_q == 0 || max_q_len == 0) return ok();
@@ -573,6 +594,27 @@ int32_t prefill_impl(void* out, const void* q, const void* k_pool, const void* v
     return fail(PAGED_ERR_INVALID_ARG, "NULL pointer");
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
     return fail(PAGED_ERR_INVALID_ARG, "misaligned pointer");
+  // The largest workgroup row count (eight waves of 32 rows) gives the fewest
+  // items; four-wave launches have at most twice as many.
+  const int64_t items = (static_cast<int64_t>(max_q_len) * (num_q_heads / num_kv_heads) + 63) / 64 *
+                        num_kv_heads * batch;
+  if (items > (1LL << 30)) return fail(PAGED_ERR_INVALID_ARG, "problem too large");
+  return ok();
+}
+
+int32_t prefill_impl(void* out, const void* q, const void* k_pool, const void* v_pool,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* cu_q_lens, const int32_t* seq_lens, int32_t batch,
+                     int32_t total_q, int32_t max_q_len, int32_t num_q_heads,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                     int32_t num_blocks, float scale, float k_scale, float v_scale,
+                     int32_t sliding_window, int esz, void* stream, int waves) {
+  if (int32_t rc = prefill_check(out, q, k_pool, v_pool, block_tables, max_blocks_per_seq,
+                                 cu_q_lens, seq_lens, batch, total_q, max_q_len, num_q_heads,
+                                 num_kv_heads, head_dim, block_size, num_blocks, scale, k_scale,
+                                 v_scale, sliding_window))
+    return rc;
+  if (batch == 0 || total_q == 0 || max_q_len == 0) return ok();
   const int group = num_q_heads / num_kv_heads;
   const int nw = (waves == 4 || waves == 8) && head_dim < 256 ? waves : default_waves(head_dim);
   const int tm = nw * rows_per_wave(head_dim);

@@ -33,11 +33,15 @@
  *   - Device pointers must be 16-byte aligned. Table and length contents live
  *     on the device and are not read by the host; the kernels never dereference
  *     a physical block id outside [1, num_blocks) nor a table column outside
- *     [0, max_blocks_per_seq) -- a token whose entry is out of range counts as
- *     absent (written nowhere, attended by nobody).
+ *     [0, max_blocks_per_seq). A key whose table entry is 0, out of range or
+ *     past the table's width is absent: attention gives it weight zero (a
+ *     query whose keys are all absent gets zeros) and the gather leaves its
+ *     output rows untouched. Well-formed tables (the allocator's) never map
+ *     an attended position to such an entry.
  *   - Pool layout: pool[num_blocks][num_kv_heads][block_size][head_dim],
  *     K and V in two separate buffers, element type given by `dtype`.
- *     Block 0 is the null sentinel and is never read.
+ *     Block 0 is the null sentinel shared by every sliding table: no kernel
+ *     reads or writes it (a write slot inside block 0 counts as padding).
  *   - A slot is physical_block * block_size + offset (int64); slot < 0 means
  *     padding.
  *   - head_dim in {64, 128, 256, 512} (512: bf16 or FP8 pools, not float32);
@@ -90,10 +94,11 @@ const char* paged_last_error(void);
  * K/V write); dtype PAGED_F32, PAGED_BF16, or PAGED_FP8_E4M3 to copy codes
  * that are already quantized (paged_kv_write_fp8 quantizes). For every t in
  * [0, num_tokens) with
- * 0 <= slot_mapping[t] < num_blocks * block_size:
+ * block_size <= slot_mapping[t] < num_blocks * block_size:
  *   k_pool[slot / block_size][h][slot % block_size][:] = new_k[t][h][:]
- * for every KV head h, and the same for V. Tokens with a negative or
- * out-of-range slot write nothing. Bytes are copied unchanged.
+ * for every KV head h, and the same for V. Tokens with a negative slot, a
+ * slot inside block 0 (the null sentinel) or an out-of-range slot write
+ * nothing. Bytes are copied unchanged.
  *   k_pool, v_pool : device, [num_blocks][num_kv_heads][block_size][head_dim]
  *   new_k, new_v   : device, [num_tokens][num_kv_heads][head_dim]
  *   slot_mapping   : device, int64 [num_tokens]
@@ -141,13 +146,22 @@ int32_t paged_kv_gather(void* out_k, void* out_v, const void* k_pool, const void
 
 /* Partition size (tokens per split-K partition) that paged_attn_decode uses
  * when called with partition_tokens == 0, for these arguments and dtype.
- * bf16: the smallest power-of-two multiple of the workgroup's stage span
- * (16 tokens per wave, 8 waves, 4 at head_dim 256 and 512) that keeps every wave
- * slot of the device busy with whole stages (never below the block size).
- * fp32: the largest power of two in [64, 1024] that still gives at least 4
- * workgroups per compute unit, else 64. A pure function of its arguments and
- * the device's compute-unit count, so a given call reproduces exactly.
- * Needs a device (PAGED_ERR_HIP otherwise). */
+ * With G = num_q_heads / num_kv_heads, span = max_seq_len (with a window:
+ * min(max_seq_len, sliding_window + block_size - 1)) and CUs = the device's
+ * compute units:
+ *   bf16 and FP8 pools: a workgroup is 4 waves streaming 16-token stages over
+ *     GT = the largest divisor of G up to 16 query heads; pairs = batch *
+ *     num_kv_heads * (G / GT); wave slots = CUs * (4 at head_dim >= 256, 12
+ *     for FP8 pools up to head_dim 128, else 8); s = ceil(pairs *
+ *     ceil(span / 16) / wave slots) rounded up to a power of two (at least 1);
+ *     partition = max(max(16, block_size), min(65536, 64 * s)).
+ *   fp32 pools: GT = the largest of 4, 2, 1 dividing G; the largest power of
+ *     two c in [64, 1024] with pairs * ceil(span / c) >= 4 * CUs (else 64), at
+ *     least block_size.
+ * The workspace then holds batch * num_q_heads * ceil(span / partition) *
+ * (head_dim + 2) floats, none when that ceiling is 1. A pure function of the
+ * arguments and the CU count, so a given call reproduces exactly. Needs a
+ * device (PAGED_ERR_HIP otherwise). */
 int32_t paged_attn_decode_partition_tokens(int32_t batch, int32_t num_q_heads,
                                            int32_t num_kv_heads, int32_t head_dim,
                                            int32_t block_size, int32_t max_seq_len,
@@ -169,7 +183,8 @@ int32_t paged_attn_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
  * [lo, n) with n = seq_lens[b], lo = max(0, n - sliding_window) when
  * sliding_window > 0 else 0 (perf doc, knobs table: batched paged decode;
  * paged-cache doc, hybrid coordinator paragraph: sliding groups and the null
- * sentinel). Per query head h (KV head h / G):
+ * sentinel). Per query head h (KV head h / G), with scale finite and > 0
+ * (PAGED_ERR_INVALID_ARG otherwise):
  *   o[b][h] = sum_t softmax_t(scale * q[b][h] . K[t]) V[t]
  * A row with n == 0 gives zeros. Long rows are split into partitions of
  * `partition_tokens` positions counted from the first live block of the row
@@ -216,7 +231,7 @@ int32_t paged_attn_decode_fp8(void* out, const void* q, const void* k_pool, cons
  * [lo, a], lo = max(0, a - sliding_window + 1) when sliding_window > 0 else 0
  * (causal inside the chunk). bf16 only; the products run on MFMA with float32
  * accumulation, probabilities rounded to bf16 for the P.V product. scale must
- * be finite and >= 0 (PAGED_ERR_INVALID_ARG otherwise); q, K and V must be
+ * be finite and > 0 (PAGED_ERR_INVALID_ARG otherwise); q, K and V must be
  * finite (NaN inputs give unspecified results).
  *   out, q       : device bf16, [total_q][num_q_heads][head_dim]
  *   cu_q_lens    : device int32 [batch + 1], cu_q_lens[0] = 0, nondecreasing,
@@ -309,7 +324,11 @@ int32_t paged_trace_durations(int32_t kernel, double* ms, int64_t capacity, int6
  * Policy: block 0 is the null sentinel (never handed out). Free blocks form a
  * FIFO, initially `free_order` (a permutation of 1..num_blocks-1 drawn by the
  * caller; NULL = ascending); allocation pops the head, freed unpublished
- * blocks join the tail. Publishing enters a full block in the prefix table
+ * blocks join the tail. The caller passes the permutation itself rather than
+ * a seed: the physical placement then follows whatever generator the caller
+ * uses (the test and benchmark inputs draw it with numpy's default_rng), and
+ * the library and any reference allocator agree on it without both having
+ * to implement one generator's permutation algorithm. Publishing enters a full block in the prefix table
  * under the exact key (domain, parent chain id, the block's token ids) and
  * gives it a fresh chain id (never reused). A published block whose refcount
  * reaches 0 joins the LRU tail and stays matchable; when the free list is

@@ -137,9 +137,10 @@ def test_partition_count_limit():
 def test_mixed_step_argument_errors():
     L = pk.lib
 
-    def call(B=3, nd=2, T=10, d=128, dt=pk.PAGED_BF16, ks=1.0, vs=1.0, part=64, ws=None, wsb=0, ptr=None):
-        return L.paged_attn_mixed(ptr, ptr, ptr, ptr, ptr, 4, ptr, ptr, B, nd, T, 8, 8, 8, d, 16, 8, 0.1, ks, vs,
-                                  0, part, 64, ws, wsb, dt, None)
+    def call(B=3, nd=2, T=10, d=128, dt=pk.PAGED_BF16, ks=1.0, vs=1.0, part=64, ws=None, wsb=0, ptr=None,
+             msl=64, scale=0.1):
+        return L.paged_attn_mixed(ptr, ptr, ptr, ptr, ptr, 4, ptr, ptr, B, nd, T, 8, 8, 8, d, 16, 8, scale, ks, vs,
+                                  0, part, msl, ws, wsb, dt, None)
 
     assert call(dt=pk.PAGED_F32) == pk.PAGED_ERR_DTYPE
     assert call(nd=4) == pk.PAGED_ERR_INVALID_ARG           # more decode rows than rows
@@ -149,8 +150,26 @@ def test_mixed_step_argument_errors():
     assert call() == pk.PAGED_ERR_INVALID_ARG               # NULL pointers
     # everything below is rejected before any device call
     assert call(d=384, ptr=16) == pk.PAGED_ERR_INVALID_ARG  # no kernel for head_dim 384
-    assert call(ptr=16, part=32) == pk.PAGED_ERR_CAPACITY   # two partitions: a workspace is needed
+    assert call(ptr=16, part=32) == pk.PAGED_ERR_INVALID_ARG  # two partitions: a workspace is needed
     assert b"workspace" in pk.lib.paged_last_error()
+    assert call(ptr=16, part=32, ws=16, wsb=64) == pk.PAGED_ERR_CAPACITY  # too small a workspace
+    assert b"workspace" in pk.lib.paged_last_error()
+    assert call(ptr=16, part=32, ws=8, wsb=1 << 20) == pk.PAGED_ERR_INVALID_ARG  # misaligned workspace
+    # the decode rows' limits are checked before the chunk rows are enqueued
+    assert call(ptr=16, part=16, msl=65536 * 16, ws=16, wsb=1 << 40) == pk.PAGED_ERR_INVALID_ARG
+    assert b"65535" in pk.lib.paged_last_error()
+    assert call(ptr=16, scale=0.0) == pk.PAGED_ERR_INVALID_ARG  # scale must be positive
+
+
+def test_scale_must_be_positive():
+    L = pk.lib
+    for scale in (0.0, -0.5, float("nan"), float("inf")):
+        rc = L.paged_attn_decode(16, 16, 16, 16, 16, 4, 16, 2, 4, 2, 128, 16, 8, scale, 0, 64, 64, None, 0,
+                                 pk.PAGED_BF16, None)
+        assert rc == pk.PAGED_ERR_INVALID_ARG and b"scale" in L.paged_last_error()
+        rc = L.paged_attn_prefill_chunk(16, 16, 16, 16, 16, 4, 16, 16, 1, 8, 8, 4, 2, 128, 16, 8, scale, 0,
+                                        pk.PAGED_BF16, None)
+        assert rc == pk.PAGED_ERR_INVALID_ARG and b"scale" in L.paged_last_error()
 
 
 def test_library_rule_needs_a_device_here():

@@ -12,6 +12,7 @@ import pytest
 
 import runner
 import synth
+import oracle
 from oracle import RefAllocator
 
 pytestmark = pytest.mark.gpu
@@ -118,6 +119,30 @@ def test_write_skips_padding_and_out_of_range_slots(pk):
     assert torch.equal(k[1, :, 1], new[0].cpu()) and torch.equal(k[3, :, 15], new[3].cpu())
     assert int(torch.isnan(k).sum()) == (4 * 16 - 2) * 2 * 64
     assert torch.equal(vp.cpu()[1, :, 1], -new[0].cpu())
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_write_leaves_the_null_block_alone(pk, dtype):
+    """Slots inside block 0 (the shared null sentinel) write nothing: whole
+    pools bit-exact against the oracle's write, NaN canaries everywhere else."""
+    import torch
+
+    announce(f"write null block {dtype}")
+    rng = np.random.default_rng(5)
+    nb, hkv, bs, d, T = 6, 2, 16, 128, 7
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    kp = torch.full((nb, hkv, bs, d), float("nan"), dtype=dt, device="cuda")
+    vp = torch.full_like(kp, float("nan"))
+    x = torch.from_numpy(rng.standard_normal((T, hkv, d)).astype(np.float32)).to(dt).cuda()
+    slots = [0, 17, 15, 5 * 16 + 3, 8, -1, 2 * 16]   # 0, 15 and 8 lie in block 0
+    pk.paged_kv_write(kp, vp, x, -x, torch.tensor(slots, dtype=torch.int64, device="cuda"))
+    torch.cuda.synchronize()
+    ek, ev = oracle.kv_write(kp.float().cpu().numpy() * np.nan, vp.float().cpu().numpy() * np.nan,
+                             x.float().cpu().numpy(), -x.float().cpu().numpy(), slots, bs)
+    got_k, got_v = kp.float().cpu().numpy(), vp.float().cpu().numpy()
+    assert np.all(np.isnan(got_k[0])) and np.all(np.isnan(got_v[0]))
+    np.testing.assert_array_equal(got_k, ek)
+    np.testing.assert_array_equal(got_v, ev)
 
 
 @pytest.mark.parametrize("name,kw", [
@@ -564,3 +589,74 @@ def test_step_graph_replays_match_eager(pk, name, kw):
     pk.trace_enable(False)
     ms, n = pk.trace_query(kern)
     assert n == 1 and ms > 0.0 and torch.equal(out, eager)
+
+
+# --------------------------------------------------------------- absent table entries
+@pytest.mark.parametrize("kind", ["decode", "prefill", "mixed"])
+@pytest.mark.parametrize("d", [128, 256])
+def test_absent_entries_get_no_weight(pk, kind, d):
+    """Table entries that are 0, past num_blocks, or columns past the table's
+    width, inside the attended range: decode, prefill and the mixed step all
+    treat those keys as absent (weight zero). Expected: the oracle's plain
+    attention over the keys that remain."""
+    import torch
+
+    announce(f"absent entries {kind} D={d}")
+    rng = np.random.default_rng(31)
+    bs, hq, hkv, nb, mb = 16, 4, 2, 40, 6
+    lens = [100, 75]                        # row 0 needs 7 blocks: column 6 lies past the width
+    chunks = {"decode": [1, 1], "prefill": [20, 10], "mixed": [1, 10]}[kind]
+    perm = list(rng.permutation(np.arange(1, nb)))
+    tables = np.zeros((2, mb), dtype=np.int32)
+    flat_k, flat_v = [], []
+    kp = np.full((nb, hkv, bs, d), np.nan, dtype=np.float32)
+    vp = kp.copy()
+    for b, n in enumerate(lens):
+        fk = synth.round_bf16(rng.standard_normal((n, hkv, d)).astype(np.float32))
+        fv = synth.round_bf16(rng.standard_normal((n, hkv, d)).astype(np.float32))
+        flat_k.append(fk)
+        flat_v.append(fv)
+        for j in range(min(mb, -(-n // bs))):
+            tables[b, j] = perm.pop()
+            kp[tables[b, j], :, :min(bs, n - j * bs)] = fk[j * bs:(j + 1) * bs].transpose(1, 0, 2)
+            vp[tables[b, j], :, :min(bs, n - j * bs)] = fv[j * bs:(j + 1) * bs].transpose(1, 0, 2)
+    tables[0, 2] = 0            # a null entry inside row 0's range
+    tables[1, 1] = nb + 5       # an out-of-range block id inside row 1's range
+    absent = [set(range(32, 48)) | set(range(96, 100)), set(range(16, 32))]
+    kp = np.nan_to_num(kp, nan=0.0)      # never-written slots of used blocks hold zeros
+    vp = np.nan_to_num(vp, nan=0.0)
+    kp[0] = np.nan                       # the null block: must never be read
+    vp[0] = np.nan
+    T = sum(chunks)
+    q = synth.round_bf16(rng.standard_normal((T, hq, d)).astype(np.float32))
+    scale = 1.0 / np.sqrt(d)
+    expect = np.zeros((T, hq, d))
+    row = 0
+    for b, n in enumerate(lens):
+        for i in range(chunks[b]):
+            a = n - chunks[b] + i
+            keep = [p for p in range(a + 1) if p not in absent[b]]
+            for h in range(hq):
+                expect[row, h] = oracle.attend_one(q[row, h], flat_k[b][keep, h // (hq // hkv)],
+                                                   flat_v[b][keep, h // (hq // hkv)], scale)
+            row += 1
+    dev = lambda x, dt=torch.bfloat16: torch.from_numpy(np.ascontiguousarray(x)).to(dt).cuda()  # noqa: E731
+    k_d, v_d, q_d = dev(kp), dev(vp), dev(q)
+    t_d = dev(tables, torch.int32)
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(chunks)]), dtype=torch.int32, device="cuda")
+    out = torch.full_like(q_d, float("nan"))
+    part = 32
+    ws_bytes = pk.paged_attn_decode_workspace_bytes(2, hq, hkv, d, bs, 128, 0, part, "bf16")
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+    if kind == "decode":
+        pk.paged_attn_decode(out, q_d, k_d, v_d, t_d, sl, scale, 128, partition_tokens=part, workspace=ws)
+    elif kind == "prefill":
+        pk.paged_attn_prefill_chunk(out, q_d, k_d, v_d, t_d, cu, sl, max(chunks), scale)
+    else:
+        pk.paged_attn_mixed(out, q_d, k_d, v_d, t_d, cu, sl, 1, max(chunks), scale, 128, partition_tokens=part,
+                            workspace=ws)
+    torch.cuda.synchronize()
+    max_abs, rel = runner.compare(out, expect, "bf16")
+    assert np.all(np.isfinite(out.float().cpu().numpy()))
+    assert runner.within("bf16", max_abs, rel), f"max_abs={max_abs:.3g} rel_l2={rel:.3g}"
