@@ -1,32 +1,36 @@
 #!/usr/bin/env python3
-"""Benchmark one step of the paged-KV hot path on one MI355X.
+"""Benchmark the paged-KV hot path on one MI355X.
 
 A step is one pass of the whole hot path over one batch: the slot-mapped KV
 write of the step's new tokens, then attention for every layer of the
 workload (split-K decode + reduce, or the chunked-prefill kernel). Inputs are
 seeded synthetic data (``synth``) already resident in HBM when timing starts.
 
-Default workload: the Qwen3-0.6B-shaped decode step (B=4, Hq=16, Hkv=8,
-D=128, bf16, 2048-token contexts with a 512-token shared prefix chain, a
-2048 MiB pool). Its 26 MiB of live K/V would fit the GPU's last-level cache, so
-the pool holds several independent batches ("waves", each with its own
-prefix chain) and consecutive steps serve different ones; a step still
-processes exactly one batch.
+Default (``--workload headline``): the two halves of the metric in one line.
+  * Decode: the Gemma-style hybrid step (B=8, Hq=8, Hkv=1, head_dim 256, bf16,
+    32768-token rows; a sliding layer with W=512 and its own pool, a full layer,
+    a KV-shared layer reading the full layer's pool), the largest decode
+    configuration. ``value`` is its step throughput (algorithmic bytes per
+    step time) and ``roofline`` its decode kernels (partial + reduce).
+  * Prefill: the 2048-token chunk over a 63488-token paged prefix (Hq=32,
+    Hkv=8, head_dim 128), reported as ``roofline_prefill``.
+Other workloads run alone with ``--workload NAME``.
 
-Prints one JSON line: the step throughput (``value``), a roofline entry for
-the dominant kernel (its average launch time from HIP events recorded by the
-library on the launch stream over the timed region) and the CPU oracle's rate
-on a bounded sample of the same workload.
+Kernel times come from HIP events the library records around each launch on
+the launch stream (``paged_trace_*``), over at least 50 steps launched eagerly
+with a 1 GiB read before every attention launch, so the caches hold unrelated
+data (``--warm`` drops the scrub); the same steps back to back without it are
+reported as ``roofline_warm``. The step throughput times K steps captured as
+one HIP graph. ``cpu_baseline`` times the float64 oracle on a bounded sample.
 
-    python bench.py [--workload qwen3|mixed|hybrid|prefill|hprefill|mixedstep|tiny] [--kv bf16|fp8]
-                    [--head-dim D] [--scrub] [--steps K] [--warmup W]
+    python bench.py [--workload headline|qwen3|mixed|hybrid|prefill|hprefill|mixedstep|tiny]
+                    [--kv bf16|fp8] [--head-dim D] [--partition-tokens P] [--warm]
+                    [--steps K] [--warmup W]
 
 ``--kv fp8`` runs the same workload over FP8 (E4M3) pools with per-layer
 scales (quantizing write, FP8 decode/prefill); the decode byte count then
 counts one byte per K/V element. ``--head-dim`` changes the workload's head
 dimension (e.g. 512 for the Gemma-style hybrid decode or prefill).
-``--scrub`` reads 1 GiB before every timed attention launch, so the
-per-kernel times are taken with caches holding unrelated data.
 """
 
 from __future__ import annotations
@@ -42,12 +46,24 @@ import numpy as np
 
 METRIC = "paged decode attn: KV GB/s & % HBM peak; prefill-chunk TFLOP/s & % MFMA"
 ROOT = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = {"decode_partial": ["decode.hip", "device.h"], "prefill": ["prefill.hip", "device.h"]}
+KERNEL_SOURCES = {"decode_partial": ["decode.hip", "device.h"], "decode_reduce": ["decode.hip", "device.h"],
+                  "prefill": ["prefill.hip", "device.h"]}
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 DEFAULT_WAVES = {"qwen3": 16}
 DEFAULT_STEPS = {"qwen3": 1000, "mixed": 200, "hybrid": 200, "prefill": 30, "hprefill": 30, "mixedstep": 100,
                  "tiny": 500}
+MIN_KERNEL_STEPS = 50           # eager steps of each per-kernel timing pass
+WORKLOAD_TITLES = {
+    "qwen3": "qwen3-0.6b-shaped decode step (B=4, Hq=16, Hkv=8, D=128, 2048-token rows, 512-token shared prefix)",
+    "mixed": "mixed-length continuous-batching decode (B=32, Hq=32, Hkv=8, D=128, rows U[128, 8192], 4 prefixes)",
+    "hybrid": "gemma-style hybrid decode: sliding (W=512) + full + kv-shared layers "
+              "(B=8, Hq=8, Hkv=1, D=256, 32768-token rows)",
+    "prefill": "chunked prefill: a 2048-token chunk over a 63488-token paged prefix (Hq=32, Hkv=8, D=128)",
+    "hprefill": "gemma-style hybrid chunked prefill: sliding + full + kv-shared layers",
+    "mixedstep": "continuous-batching step: decode rows + a prefill chunk in one call",
+    "tiny": "tiny fp32 decode",
+}
 
 
 def log(msg):
@@ -294,57 +310,97 @@ def _subset(wl, rows):
     return sub
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="qwen3", choices=["qwen3", "mixed", "hybrid", "prefill", "hprefill", "mixedstep", "tiny"])
-    ap.add_argument("--waves", type=int, default=None, help="independent batches rotated through")
-    ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"], help="KV pool element type")
-    ap.add_argument("--head-dim", type=int, default=None, help="head_dim override (e.g. 512 for the hybrid decode)")
-    ap.add_argument("--partition-tokens", type=int, default=None,
-                    help="decode split-K partition size (default: the workload's, else the library rule)")
-    ap.add_argument("--scrub", action="store_true",
-                    help="read a 1 GiB buffer before every attention launch of the per-kernel timing pass, "
-                         "so the roofline is taken with cold caches")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="run only a plain 256 MiB device copy (scales HBM byte counters)")
-    args = ap.parse_args()
+def counter_traffic_step(kern_counts, tag):
+    """HBM bytes of one step's launches of the given kernels ({kernel: launches
+    per step}) from the recorded counters, or None if any is missing or stale."""
+    tot = 0
+    for kern, n in kern_counts.items():
+        t = counter_traffic(kern, tag)
+        if t is None:
+            return None
+        tot += t * n
+    return tot
 
-    if args.copy_calibration:
-        copy_calibration()
-        return
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only; a multi-GPU run is not available "
-              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
-        sys.exit(2)
 
+def timed_pass(pk, stream, calls, first, steps, n_writes, scrub):
+    """Launch ``steps`` steps eagerly with the library's launch events on;
+    with ``scrub``, read 1 GiB before every attention launch (a read leaves
+    the caches holding clean, unrelated lines; a write would leave dirty ones
+    whose write-back the next kernel would pay). Returns {kernel: [ms, ...]}."""
     import torch
 
-    import block_paged_kv_amd as pk
+    R = len(calls)
+    if scrub:
+        scrub_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        sink = torch.zeros((), dtype=torch.float32, device="cuda")
+    pk.trace_reset()
+    torch.cuda.synchronize()
+    pk.trace_enable(True)
+    with torch.cuda.stream(stream):
+        for i in range(steps):
+            for j, c in enumerate(calls[(first + i) % R]):
+                if scrub and j >= n_writes:
+                    pk.trace_enable(False)
+                    sink.copy_(scrub_buf.sum())
+                    pk.trace_enable(True)
+                c()
+    torch.cuda.synchronize()
+    pk.trace_enable(False)
+    return {k: list(pk.trace_durations(k)) for k in pk.KERNELS}
+
+
+def _pcts(ms):
+    if not ms:
+        return None
+    return [round(float(x) * 1e3, 3) for x in np.percentile(np.asarray(ms), [10, 50, 90])]
+
+
+def roofline_entry(kernels, durations, steps, work_per_step, bound, traffic=None, extra=None):
+    """Roofline of the kernels named in ``kernels`` taken together: their
+    summed launch durations per step against the step's algorithmic work."""
+    total_ms = sum(sum(durations.get(k, [])) for k in kernels)
+    per_step_ms = total_ms / max(steps, 1)
+    if bound == "hbm":
+        achieved = work_per_step / (per_step_ms * 1e-3) / 1e9
+        peak, unit = HBM_PEAK_GBS, "GB/s"
+    else:
+        achieved = work_per_step / (per_step_ms * 1e-3) / 1e12
+        peak, unit = MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+    e = {"kernel": "+".join(kernels), "bound": bound, "achieved": round(achieved, 3), "peak": peak,
+         "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic,
+         "kernel_us_per_step": round(per_step_ms * 1e3, 3),
+         "avg_launch_us": {k: round(float(np.mean(durations[k])) * 1e3, 3) for k in kernels if durations.get(k)},
+         "launch_us_p10_p50_p90": {k: _pcts(durations.get(k)) for k in kernels if durations.get(k)},
+         "launches": {k: len(durations.get(k, [])) for k in kernels},
+         "work_per_step": work_per_step}
+    if extra:
+        e.update(extra)
+    return e
+
+
+def run_part(pk, args, name, steps, warmup):
+    """Build workload ``name``, time its steps (graph) and its kernels (eager,
+    scrubbed and warm); return the fields of a bench line for it."""
+    import torch
+
     import runner
     import synth
 
-    steps = args.steps or DEFAULT_STEPS[args.workload]
-    waves = args.waves or DEFAULT_WAVES.get(args.workload, 1)
-    kw = {"waves": waves} if args.workload == "qwen3" else {}
-    if args.kv == "fp8":
-        if args.workload == "tiny":
+    waves = args.waves or DEFAULT_WAVES.get(name, 1)
+    kw = {"waves": waves} if name == "qwen3" else {}
+    fp8 = args.kv == "fp8"
+    if fp8:
+        if name == "tiny":
             print("bench.py: --kv fp8 needs a bf16 workload (not tiny)", file=sys.stderr)
             sys.exit(2)
         kw["kv_dtype"] = "fp8"
-    fp8 = args.kv == "fp8"
     if args.head_dim:
         kw["head_dim"] = args.head_dim
     if args.partition_tokens is not None:
         kw["part"] = args.partition_tokens
-    log(f"[bench] building workload {args.workload} ({kw})")
-    wl = synth.make(args.workload, **kw)
-    R = waves if args.workload == "qwen3" else 1
+    log(f"[bench] building workload {name} ({kw})")
+    wl = synth.make(name, **kw)
+    R = waves if name == "qwen3" else 1
     mixed_step = wl.kind == "prefill" and wl.num_decode > 0
     wsz = wl.wave_size or wl.batch
     tabs = synth.build_tables(pk.Allocator, wl)
@@ -417,9 +473,9 @@ def main():
             c()
 
     stream.wait_stream(torch.cuda.current_stream())
-    log(f"[bench] warmup {args.warmup} steps")
+    log(f"[bench] {name}: warmup {warmup} steps")
     with torch.cuda.stream(stream):
-        for i in range(args.warmup):
+        for i in range(warmup):
             step(i)
     torch.cuda.synchronize()
 
@@ -433,14 +489,14 @@ def main():
             graph = torch.cuda.CUDAGraph()
             with torch.cuda.graph(graph, stream=stream):
                 for i in range(steps):
-                    step(args.warmup + i)
+                    step(warmup + i)
             graph.replay()  # warm replay: instantiation and first-touch costs
             torch.cuda.synchronize()
         except Exception as e:  # noqa: BLE001
             log(f"[bench] graph capture failed ({e}); timing eager launches")
             graph = None
             timing = "eager"
-    log(f"[bench] timing {steps} steps ({timing})")
+    log(f"[bench] {name}: timing {steps} steps ({timing})")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     if graph is not None:
@@ -448,142 +504,172 @@ def main():
     else:
         with torch.cuda.stream(stream):
             for i in range(steps):
-                step(args.warmup + i)
+                step(warmup + i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / steps
+    del graph
 
-    # Timed region 2 (per-kernel durations): the same steps launched eagerly,
-    # the library recording a HIP event pair around every launch on the launch
-    # stream (events inside a captured graph cannot be timed).
-    log(f"[bench] per-kernel timing over {steps} eager steps{' (caches scrubbed)' if args.scrub else ''}")
-    if args.scrub:
-        # A read leaves the caches holding clean, unrelated lines (a write
-        # would leave dirty ones whose write-back the next kernel would pay).
-        scrub_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
-        sink = torch.zeros((), dtype=torch.float32, device="cuda")
+    # Timed regions 2 and 3 (per-kernel durations): the same steps launched
+    # eagerly, first with the caches scrubbed before every attention launch,
+    # then back to back (warm).
+    ksteps = max(steps, MIN_KERNEL_STEPS)
     n_writes = sum(1 for L in wl.layers if not L.alias_of)
-    pk.trace_reset()
-    torch.cuda.synchronize()
-    pk.trace_enable(True)
-    with torch.cuda.stream(stream):
-        for i in range(steps):
-            for j, c in enumerate(calls[(args.warmup + i) % R]):
-                if args.scrub and j >= n_writes:
-                    pk.trace_enable(False)
-                    sink.copy_(scrub_buf.sum())
-                    pk.trace_enable(True)
-                c()
-    torch.cuda.synchronize()
-    pk.trace_enable(False)
+    log(f"[bench] {name}: per-kernel timing over {ksteps} eager steps, scrubbed"
+        + ("" if args.warm else " and warm"))
+    dur_cold = timed_pass(pk, stream, calls, warmup, ksteps, n_writes, scrub=not args.warm)
+    dur_warm = dur_cold if args.warm else timed_pass(pk, stream, calls, warmup, ksteps, n_writes, scrub=False)
+    caches = "warm (back to back)" if args.warm else "scrubbed (1 GiB read before each attention launch)"
 
+    tag = name + (f"_d{args.head_dim}" if args.head_dim else "") + ("_fp8" if fp8 else "")
+    nl = len(wl.layers)
+    part = {"name": name, "wl": wl, "tabs": tabs, "ms_per_step": ms_per_step, "timing": timing,
+            "ksteps": ksteps, "caches": caches}
     extra = {}
     if mixed_step:
-        # Decode rows' KV bytes over the step time is the value; the chunk's
-        # prefill carries the dominant kernel's roofline, the decode partial a
-        # second one (both timed while they share the device).
         dec_rows = list(range(wl.num_decode))
         T = int(wl.chunk_lens.sum())
         dwork = decode_bytes(wl, tabs, dec_rows)
         pwork = prefill_flops(wl, set(range(wl.num_decode, T)))
-        value = dwork / (ms_per_step * 1e-3) / 1e9
-        unit = "GB/s"
-        kern = "prefill"
-        k_ms, k_n = pk.trace_query(kern)
-        work = pwork
-        achieved = pwork * steps / (k_ms * 1e-3) / 1e12
-        peak, bound, runit = MFMA_BF16_PEAK_TFLOPS, "mfma", "TFLOP/s"
-        d_ms, d_n = pk.trace_query("decode_partial")
-        d_ach = dwork * steps / (d_ms * 1e-3) / 1e9
+        part["value"], part["unit"] = dwork / (ms_per_step * 1e-3) / 1e9, "GB/s"
+        part["roofline"] = roofline_entry(["prefill"], dur_cold, ksteps, pwork, "mfma",
+                                          counter_traffic_step({"prefill": nl}, tag))
+        part["roofline_warm"] = roofline_entry(["prefill"], dur_warm, ksteps, pwork, "mfma")
         serial_ms = time_serial_mixed_step(pk, wl, dev, outs, ws, stream, steps)
         extra = {
-            "roofline_decode": {"kernel": "decode_partial", "bound": "hbm", "achieved": round(d_ach, 3),
-                                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(d_ach / HBM_PEAK_GBS, 4),
-                                "avg_launch_us": round(d_ms * 1e3 / max(d_n, 1), 3), "work_per_step": dwork},
+            "roofline_decode": roofline_entry(["decode_partial", "decode_reduce"], dur_cold, ksteps, dwork, "hbm"),
             "prefill_tflops_in_step": round(pwork / (ms_per_step * 1e-3) / 1e12, 3),
             "serial_ms_per_step": round(serial_ms, 6),
             "speedup_vs_serial": round(serial_ms / ms_per_step, 4),
         }
     elif wl.kind == "decode":
         per_wave = [decode_bytes(wl, tabs, list(range(r * wsz, (r + 1) * wsz))) for r in range(R)]
-        work = float(np.mean([per_wave[(args.warmup + i) % R] for i in range(steps)]))
-        value = work / (ms_per_step * 1e-3) / 1e9
-        unit = "GB/s"
-        kern = "decode_partial"
-        k_ms, k_n = pk.trace_query(kern)
-        achieved = work * steps / (k_ms * 1e-3) / 1e9  # all partial launches of the region
-        peak, bound, runit = HBM_PEAK_GBS, "hbm", "GB/s"
+        work = float(np.mean([per_wave[(warmup + i) % R] for i in range(ksteps)]))
+        step_work = float(np.mean([per_wave[(warmup + i) % R] for i in range(steps)]))
+        part["value"], part["unit"] = step_work / (ms_per_step * 1e-3) / 1e9, "GB/s"
+        n_red = len(dur_cold.get("decode_reduce", [])) // max(ksteps, 1)
+        kerns = ["decode_partial", "decode_reduce"] if n_red else ["decode_partial"]
+        traffic = counter_traffic_step({"decode_partial": nl, **({"decode_reduce": n_red} if n_red else {})}, tag)
+        part["roofline"] = roofline_entry(kerns, dur_cold, ksteps, work, "hbm", traffic,
+                                          {"traffic_per": "step"})
+        part["roofline_partial_only"] = roofline_entry(["decode_partial"], dur_cold, ksteps, work, "hbm")
+        part["roofline_warm"] = roofline_entry(kerns, dur_warm, ksteps, work, "hbm")
+        if nl > 1:
+            by = {}
+            for k in kerns:
+                dd = dur_cold.get(k, [])
+                per = len(dd) // max(ksteps, 1)
+                if per == nl:  # one launch per layer and step, in layer order
+                    by[k] = {L.name: round(float(np.mean(dd[i::nl])) * 1e3, 3) for i, L in enumerate(wl.layers)}
+            extra["kernel_us_by_layer"] = by
+            extra["work_by_layer"] = decode_kv_bytes_per_layer(wl, tabs, list(range(wsz)))
     else:
         work = prefill_flops(wl)
-        value = work / (ms_per_step * 1e-3) / 1e12
-        unit = "TFLOP/s"
-        kern = "prefill"
-        k_ms, k_n = pk.trace_query(kern)
-        achieved = work * steps / (k_ms * 1e-3) / 1e12
-        peak, bound, runit = MFMA_BF16_PEAK_TFLOPS, "mfma", "TFLOP/s"
-    kernels = {}
-    for name in pk.KERNELS:
-        ms, n = pk.trace_query(name)
-        if n:
-            kernels[name] = {"launches": n, "avg_us": round(ms * 1e3 / n, 3)}
-    if len(wl.layers) > 1:
-        # attention launches cycle through the layers in order within a step
-        dur = pk.trace_durations(kern)
-        kernels[f"{kern}_by_layer_avg_us"] = {
-            L.name: round(float(np.mean(dur[i::len(wl.layers)])) * 1e3, 3) for i, L in enumerate(wl.layers)}
-    log(f"[bench] kernels: {kernels}")
+        part["value"], part["unit"] = work / (ms_per_step * 1e-3) / 1e12, "TFLOP/s"
+        part["roofline"] = roofline_entry(["prefill"], dur_cold, ksteps, work, "mfma",
+                                          counter_traffic_step({"prefill": nl}, tag), {"traffic_per": "step"})
+        part["roofline_warm"] = roofline_entry(["prefill"], dur_warm, ksteps, work, "mfma")
+        if nl > 1:
+            dd = dur_cold.get("prefill", [])
+            extra["kernel_us_by_layer"] = {"prefill": {L.name: round(float(np.mean(dd[i::nl])) * 1e3, 3)
+                                                       for i, L in enumerate(wl.layers)}}
+    part["kernels"] = {k: {"launches": len(v), "avg_us": round(float(np.mean(v)) * 1e3, 3)}
+                       for k, v in dur_cold.items() if v}
+    part["extra"] = extra
+    part["config"] = {
+        "workload": WORKLOAD_TITLES[name] + (f", head_dim {args.head_dim}" if args.head_dim else ""),
+        "batch": int(wsz), "num_q_heads": wl.hq, "num_kv_heads": wl.hkv, "head_dim": wl.head_dim,
+        "block_size": wl.block_size, "max_seq_len": wl.max_seq_len,
+        "layers": [L.name for L in wl.layers], "waves_rotated": R,
+        "pool_blocks": [L.num_blocks for L in wl.layers if not L.alias_of],
+        "kv_dtype": "fp8_e4m3" if fp8 else wl.dtype,
+    }
+    if mixed_step:
+        part["config"]["decode_rows"] = wl.num_decode
+        part["config"]["chunk_tokens"] = [int(c) for c in wl.chunk_lens[wl.num_decode:]]
+    log(f"[bench] {name}: step {ms_per_step * 1e3:.1f} us, kernels {part['kernels']}")
+    del dev, outs, ws, calls
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return part
 
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="headline",
+                    choices=["headline", "qwen3", "mixed", "hybrid", "prefill", "hprefill", "mixedstep", "tiny"])
+    ap.add_argument("--waves", type=int, default=None, help="independent batches rotated through")
+    ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"], help="KV pool element type")
+    ap.add_argument("--head-dim", type=int, default=None, help="head_dim override (e.g. 512 for the hybrid decode)")
+    ap.add_argument("--partition-tokens", type=int, default=None,
+                    help="decode split-K partition size (default: the workload's, else the library rule)")
+    ap.add_argument("--warm", action="store_true",
+                    help="time kernels back to back only (no 1 GiB read before each attention launch)")
+    ap.add_argument("--scrub", action="store_true", help="(default; kept for older command lines)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 256 MiB device copy (scales HBM byte counters)")
+    args = ap.parse_args()
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only; a multi-GPU run is not available "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch  # noqa: F401
+
+    import block_paged_kv_amd as pk
+
+    headline = args.workload == "headline"
+    first = "hybrid" if headline else args.workload
+    steps = args.steps or DEFAULT_STEPS[first]
+    p = run_part(pk, args, first, steps, args.warmup)
     result = {
         "metric": METRIC,
-        "value": round(value, 3),
-        "unit": unit,
+        "value": round(p["value"], 3),
+        "unit": p["unit"],
         "n_gpus": 1,
         "steps": steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 6),
+        "ms_per_step": round(p["ms_per_step"], 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": wl.dtype,
+        "dtype": p["wl"].dtype,
         "data": "synthetic",
-        "config": {
-            "workload": {"qwen3": "qwen3-0.6b-shaped decode step", "mixed": "mixed-length continuous-batching decode",
-                         "hybrid": "gemma-style hybrid sliding/full/kv-shared decode",
-                         "prefill": "chunked prefill over cached prefix",
-                         "hprefill": "gemma-style hybrid sliding/full/kv-shared chunked prefill",
-                         "mixedstep": "continuous-batching step: decode rows + a prefill chunk in one call",
-                         "tiny": "tiny fp32 decode"}[args.workload],
-            "batch": int(wsz), "num_q_heads": wl.hq, "num_kv_heads": wl.hkv, "head_dim": wl.head_dim,
-            "block_size": wl.block_size, "max_seq_len": wl.max_seq_len,
-            "layers": [L.name for L in wl.layers], "waves_rotated": R,
-            "pool_blocks": [L.num_blocks for L in wl.layers if not L.alias_of],
-            "kv_dtype": "fp8_e4m3" if fp8 else wl.dtype,
-        },
-        "roofline": {
-            "kernel": kern,
-            "bound": bound,
-            "achieved": round(achieved, 3),
-            "peak": peak,
-            "unit": runit,
-            "frac": round(achieved / peak, 4),
-            "traffic": counter_traffic(kern, args.workload + (f"_d{args.head_dim}" if args.head_dim else "")
-                                       + ("_fp8" if fp8 else "")),
-            "avg_launch_us": round(k_ms * 1e3 / max(k_n, 1), 3),
-            "launch_us_p10_p50_p90": launch_percentiles(pk, kern),
-            "launches": k_n,
-            "work_per_step": work,
-        },
-        "kernels": kernels,
-        "timing": timing,
-        "kernel_timing_caches": "scrubbed (1 GiB read before each attention launch)" if args.scrub else "warm",
+        "config": p["config"],
+        "roofline": p["roofline"],
     }
-    result.update(extra)
-    if mixed_step:
-        result["config"]["decode_rows"] = wl.num_decode
-        result["config"]["chunk_tokens"] = [int(c) for c in wl.chunk_lens[wl.num_decode:]]
+    for k in ("roofline_partial_only", "roofline_warm"):
+        if k in p:
+            result[k] = p[k]
+    result.update(p["extra"])
+    result["kernels"] = p["kernels"]
+    result["timing"] = p["timing"]
+    result["kernel_timing"] = f"{p['ksteps']} eager steps, caches {p['caches']}"
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
-        result["cpu_baseline"] = cpu_baseline(wl, args)
+        result["cpu_baseline"] = cpu_baseline(p["wl"], args)
+    del p
+    if headline:
+        # The metric's second half on the same line: the chunked prefill.
+        q = run_part(pk, args, "prefill", args.steps or DEFAULT_STEPS["prefill"], args.warmup)
+        result["prefill"] = {"value": round(q["value"], 3), "unit": q["unit"],
+                             "ms_per_step": round(q["ms_per_step"], 6), "config": q["config"]}
+        result["roofline_prefill"] = q["roofline"]
+        result["roofline_prefill_warm"] = q["roofline_warm"]
+        result["kernels_prefill"] = q["kernels"]
+        if not args.no_cpu_baseline:
+            log("[bench] timing the CPU oracle on a bounded prefill sample")
+            result["cpu_baseline_prefill"] = cpu_baseline(q["wl"], args)
     print(json.dumps(result), flush=True)
 
 
