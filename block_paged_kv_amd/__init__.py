@@ -77,6 +77,8 @@ _SIGNATURES = {
     "paged_attn_decode_workspace_bytes": [_c_int32] * 9 + [ctypes.POINTER(_c_size)],
     "paged_attn_decode": [_c_void_p] * 5 + [_c_int32, _c_void_p] + [_c_int32] * 6 + [_c_float]
     + [_c_int32] * 3 + [_c_void_p, _c_size, _c_int32, _c_void_p],
+    "paged_attn_decode_noalloc": [_c_void_p] * 5 + [_c_int32, _c_void_p] + [_c_int32] * 6 + [_c_float]
+    + [_c_int32] * 4 + [_c_void_p],
     "paged_attn_prefill_chunk": [_c_void_p] * 5 + [_c_int32, _c_void_p, _c_void_p] + [_c_int32] * 8
     + [_c_float, _c_int32, _c_int32, _c_void_p],
     "paged_trace_enable": [_c_int32],
@@ -281,6 +283,25 @@ def paged_attn_decode(out, q, k_pool, v_pool, block_tables, seq_lens, scale, max
         _dev(block_tables, "block_tables", torch.int32), mb, _dev(seq_lens, "seq_lens", torch.int32, 1),
         B, hq, hkv, d, bs, nb, float(scale), int(sliding_window), int(partition_tokens),
         int(max_seq_len), ws_ptr, ws_bytes, _dtype_code(q), _stream(stream)), prepare)
+
+
+def paged_attn_decode_noalloc(out, q, k_pool, v_pool, block_tables, seq_lens, scale, max_seq_len,
+                              sliding_window=0, partition_tokens=0, stream=None, prepare=False):
+    """``paged_attn_decode`` with the partials in the library's per-GPU device
+    scratch (no workspace argument; calls that overlap on one GPU race)."""
+    torch = _torch()
+    nb, hkv, bs, d = _pool_geom(k_pool, v_pool)
+    B, hq, dq = (int(x) for x in q.shape)
+    if dq != d or tuple(out.shape) != (B, hq, d) or q.dtype != k_pool.dtype or out.dtype != q.dtype:
+        raise PagedError(PAGED_ERR_INVALID_ARG, "q/out must be [B, Hq, D] in the pool dtype")
+    if block_tables.dim() != 2 or int(block_tables.shape[0]) != B or tuple(seq_lens.shape) != (B,):
+        raise PagedError(PAGED_ERR_INVALID_ARG, "block_tables must be [B, MB] and seq_lens [B]")
+    return _invoke(lib.paged_attn_decode_noalloc, (
+        _dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+        _dev(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
+        _dev(seq_lens, "seq_lens", torch.int32, 1), B, hq, hkv, d, bs, nb, float(scale),
+        int(sliding_window), int(partition_tokens), int(max_seq_len), _dtype_code(q), _stream(stream)),
+        prepare)
 
 
 def paged_attn_prefill_chunk(out, q, k_pool, v_pool, block_tables, cu_q_lens, seq_lens, max_q_len,

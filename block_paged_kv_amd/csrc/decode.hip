@@ -30,6 +30,8 @@
 //     elements; token lanes, then waves (through LDS), merge at the end.
 
 #include <cmath>
+#include <mutex>
+#include <vector>
 
 #include "attn.h"
 #include "device.h"
@@ -1294,4 +1296,67 @@ extern "C" int32_t paged_attn_decode_fp8(void* out, const void* q, const void* k
                      num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, k_scale,
                      v_scale, sliding_window, partition_tokens, max_seq_len, workspace,
                      workspace_bytes, 1, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Decode without a caller workspace: the split-K partials live in a
+// file-scope device array, one copy per GPU for the life of the process.
+namespace pagedkv {
+namespace {
+
+constexpr size_t kScratchBytes = size_t{16} << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of this GPU's `scratch`, looked up once per device with that
+// device current (host code must never pass the array's own name to a kernel:
+// on the host it is a stand-in, not a device address).
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;
+
+int32_t scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(PAGED_ERR_HIP, "hipGetDevice failed");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (static_cast<int>(g_scratch_ptr.size()) <= dev) g_scratch_ptr.resize(dev + 1, nullptr);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(PAGED_ERR_HIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ok();
+}
+
+}  // namespace
+}  // namespace pagedkv
+
+extern "C" int32_t paged_attn_decode_noalloc(void* out, const void* q, const void* k_pool,
+                                             const void* v_pool, const int32_t* block_tables,
+                                             int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                             int32_t batch, int32_t num_q_heads,
+                                             int32_t num_kv_heads, int32_t head_dim,
+                                             int32_t block_size, int32_t num_blocks, float scale,
+                                             int32_t sliding_window, int32_t partition_tokens,
+                                             int32_t max_seq_len, int32_t dtype, void* stream) {
+  if (dtype != PAGED_F32 && dtype != PAGED_BF16)
+    return fail(PAGED_ERR_DTYPE, "paged_attn_decode_noalloc takes f32 or bf16, got %d", dtype);
+  size_t need = 0;
+  if (int32_t rc = paged_attn_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim,
+                                                     block_size, max_seq_len, sliding_window,
+                                                     partition_tokens, dtype, &need))
+    return rc;
+  if (need > kScratchBytes)
+    return fail(PAGED_ERR_CAPACITY,
+                "paged_attn_decode_noalloc: these arguments need %zu bytes of partials, more than "
+                "the library's %zu-byte device scratch (use paged_attn_decode with a workspace)",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  if (need > 0)
+    if (int32_t rc = scratch_address(&ws)) return rc;
+  return decode_impl(out, q, k_pool, v_pool, block_tables, max_blocks_per_seq, seq_lens, batch,
+                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, 1.f, 1.f,
+                     sliding_window, partition_tokens, max_seq_len, ws, need > 0 ? kScratchBytes : 0,
+                     esize_of(dtype), stream);
 }

@@ -222,6 +222,26 @@ int32_t paged_attn_decode_fp8(void* out, const void* q, const void* k_pool, cons
                               int32_t max_seq_len, void* workspace, size_t workspace_bytes,
                               void* stream);
 
+/* paged_attn_decode for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. The
+ * same kernels and partitions as paged_attn_decode (f32 or bf16 pools), with
+ * the split-K partials in a device array the library holds per GPU (16 MiB,
+ * kept until the process ends) instead of a caller workspace; the caller
+ * still passes inputs and outputs. Nothing is allocated by the call.
+ * PAGED_ERR_CAPACITY when the partials need more than 16 MiB
+ * (paged_attn_decode_workspace_bytes gives the need for the same arguments).
+ * The partials need no clearing between calls: every partition a row uses is
+ * written before the reduce reads it. Every call on one GPU shares that
+ * array: calls that overlap on one GPU (several streams, several host
+ * threads) race on it and give wrong results. */
+int32_t paged_attn_decode_noalloc(void* out, const void* q, const void* k_pool, const void* v_pool,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                  int32_t num_blocks, float scale, int32_t sliding_window,
+                                  int32_t partition_tokens, int32_t max_seq_len, int32_t dtype,
+                                  void* stream);
+
 /* Chunked-prefill attention over a cached paged prefix (perf doc, knobs table:
  * prefill chunk size; the paged-attention bridge for prefill over a cache hit
  * that reads K/V through the pages). Row b owns query rows
