@@ -163,11 +163,9 @@ def test_fp8_prefill_small(pk, kw):
     run_case(pk, synth.make("prefill", kv_dtype="fp8", **kw), label="fp8-prefill")
 
 
-def test_fp8_prefill_full_size_sampled_rows(pk):
-    wl = synth.make("prefill", kv_dtype="fp8")
-    rows = sorted(set([0, 1, 31, 32, 127, 128, 1023, 1024, 2047] +
-                      list(np.random.default_rng(6).integers(0, 2048, size=24))))
-    run_case(pk, wl, rows=rows, label="fp8-prefill-full")
+@pytest.mark.timeout(600)  # the whole output against the float64 oracle on the host
+def test_fp8_prefill_full_size_every_row(pk):
+    run_case(pk, synth.make("prefill", kv_dtype="fp8"), label="fp8-prefill-full")
 
 
 def test_plain_entry_points_reject_fp8_pools(pk):
