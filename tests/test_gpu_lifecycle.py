@@ -100,18 +100,24 @@ def test_request_lifecycle_prefix_reuse_grow_and_eviction(pk):
     check([1])
 
     # B: A's first 48 tokens, then 12 of its own; the prefix is found, the new
-    # block does not fit until the pools grow
+    # block does not fit: with a maximum of 16 blocks the reservation asks for
+    # growth to min(16, max(2 * 8, 8 + 1)) = 16 blocks, the pools grow, and the
+    # one retry reserves
     tok_b = tok_a[:48] + list(range(2000, 2012))
     kb_own, vb_own = kv(12)
     both("add", 2)
     assert both("match_prefix", 2, tok_b, DOM) == 48
     both_fail("reserve", 2, 60)
+    both_fail("reserve_or_grow", 2, 60)          # a fixed pool (maximum = size) cannot grow
+    both("set_max_blocks", 16)
+    grow_to = both("reserve_or_grow", 2, 60)
+    assert grow_to == 16 and cpp.num_free() == (0, 0)
     for name in "kv":
-        bigger = torch.zeros((16, HKV, BS, D), dtype=torch.bfloat16, device=dev)
+        bigger = torch.zeros((grow_to, HKV, BS, D), dtype=torch.bfloat16, device=dev)
         bigger[:8] = pools[name]
         pools[name] = bigger
-    order2 = [int(x) for x in rng.permutation(np.arange(8, 16))]
-    both("grow", 16, order2)
+    order2 = [int(x) for x in rng.permutation(np.arange(8, grow_to))]
+    both("grow", grow_to, order2)
     both("reserve", 2, 60)
     write(2, 48, kb_own, vb_own)
     both("commit_tokens", 2, tok_b[48:])
