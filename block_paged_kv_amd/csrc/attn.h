@@ -28,7 +28,7 @@ int32_t decode_check(const void* out, const void* q, const void* k_pool, const v
 
 // Chunked prefill over pools of esz-byte elements (2 bf16, 1 FP8 codes); q and
 // out bf16. cu_q_lens holds absolute offsets into q and out. waves: 4 or 8
-// waves per workgroup up to head_dim 128 (head_dim 256 takes 8, 512 takes 4
+// waves per workgroup up to head_dim 128 (head_dim 256 and 512 take 8
 // whatever is asked), 0 for the default.
 int32_t prefill_impl(void* out, const void* q, const void* k_pool, const void* v_pool,
                      const int32_t* block_tables, int32_t max_blocks_per_seq,

@@ -10,8 +10,9 @@
 //   * Query rows are (position, query head) pairs of one KV head, packed
 //     position-major, so the G query heads sharing a KV head share every K/V
 //     tile. A wave owns 32 rows up to head_dim 128 and 16 beyond; a
-//     workgroup has eight waves (four at head_dim 512, and inside the mixed
-//     step).
+//     workgroup has eight waves (four inside the mixed step up to head_dim
+//     128). At head_dim 512 the waves come in pairs over the same 16 rows,
+//     each holding half of head_dim.
 //   * K/V tiles of 64 keys (32 at head_dim 512) are staged in LDS, both
 //     row-major (key, head_dim); the P.V operand is read with a transposing
 //     LDS read (ds_read_b64_tr_b16), which hands each lane consecutive keys.
@@ -41,15 +42,21 @@ constexpr int rows_per_wave(int d) { return d >= 256 ? 16 : 32; }
 // Keys per K/V tile: 64, except 32 at head_dim 512, where two buffers of 64
 // one-KiB key rows (K and V) would not fit in a CU's 160 KiB of LDS.
 constexpr int tile_keys(int d) { return d >= 512 ? 32 : 64; }
+// Waves that share a set of query rows and split the head dimension between
+// them: two at head_dim 512, one below. Each of the two holds half of the
+// query operands, computes the partial scores over its half, exchanges them
+// with its partner through LDS, and accumulates half of the output columns:
+// the accumulators of 16 rows x 256 columns and half the query operands fit
+// two waves per SIMD, where one wave holding all 512 columns needed the
+// whole register file of its SIMD.
+constexpr int splits(int d) { return d >= 512 ? 2 : 1; }
 // Waves per workgroup: eight by default (up to head_dim 128, 256 query rows
 // share each staged K/V tile and the workgroup fills a CU's registers; at
 // head_dim 256, 8 x 16 rows, two waves per SIMD, the 128 KiB of tiles allow
-// one workgroup), four at head_dim 512 (one wave per SIMD: the accumulators
-// of 16 rows x 512 columns and the query operands need more registers than
-// two waves per SIMD leave), and four up to head_dim 128 when decode
-// workgroups run beside the prefill (mixed step), so that a CU can hold one
-// of each.
-constexpr int default_waves(int d) { return d >= 512 ? 4 : 8; }
+// one workgroup; at 512, four pairs of waves over 64 rows), and four up to
+// head_dim 128 when decode workgroups run beside the prefill (mixed step), so
+// that a CU can hold one of each.
+constexpr int default_waves(int) { return 8; }
 constexpr int kNumXcd = 8;
 
 typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
@@ -80,9 +87,11 @@ __device__ __forceinline__ floatx4_t mfma16x16x32(const uint4& a, const uint4& b
 template <int D, int ESZ, int NW>
 __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill_kernel(PrefillParams a) {
   constexpr int kWaves = NW;
+  constexpr int SPL = splits(D);    // waves per set of query rows
+  constexpr int RG = NW / SPL;      // row groups of the workgroup
   constexpr int RPW = rows_per_wave(D);
   constexpr int JT = RPW / 16;  // 16-row query tiles per wave
-  constexpr int kTileM = NW * RPW;
+  constexpr int kTileM = RG * RPW;
   constexpr int kTileN = tile_keys(D);
   constexpr int NS = kTileN / 16;    // 16-key sub-tiles per tile (S^T column tiles)
   constexpr int NK = kTileN / 32;    // 32-key MFMA steps of P.V per tile
@@ -98,6 +107,8 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
   constexpr int DCH = D / 8;         // 16-byte chunks per key row
   constexpr int KS = D / 32;         // MFMA k-steps over head_dim
   constexpr int NT = D / 16;         // output column tiles
+  constexpr int KSW = KS / SPL;      // k-steps of this wave's part of head_dim
+  constexpr int NTW = NT / SPL;      // output column tiles of this wave
   constexpr int ROWB = D * 2;        // bytes per LDS key row
   constexpr float kNegInf = -INFINITY;
   auto swz_k = [](int r) { return D >= 128 ? (r & 15) : ((r >> 1) & 7); };
@@ -105,6 +116,8 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
 
   __shared__ __attribute__((aligned(16))) uint16_t k_s[2][kTileN * D];
   __shared__ __attribute__((aligned(16))) uint16_t v_s[2][kTileN * D];
+  // Partial scores handed to the partner wave (split head dimension only).
+  __shared__ floatx4_t exch[SPL > 1 ? NW : 1][SPL > 1 ? JT * (kTileN / 16) : 1][64];
 
   // XCD-aware work mapping: XCD x takes work items [x*per_xcd, (x+1)*per_xcd).
   const int lin = blockIdx.x;
@@ -133,14 +146,16 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lq = lane & 15;   // query column inside a 16-wide tile
   const int lg = lane >> 4;   // lane group 0..3
+  const int wrow = SPL > 1 ? wave % RG : wave;  // this wave's set of query rows
+  const int half = SPL > 1 ? wave / RG : 0;     // its part of head_dim
 
   // Query rows of this lane in the S^T layout: wave rows 16j + lq.
   int qpos[JT], qlo[JT];
   bool qvalid[JT];
-  uint4 qreg[JT][KS];
+  uint4 qreg[JT][KSW];
 #pragma unroll
   for (int j = 0; j < JT; ++j) {
-    const int r = r_first + wave * RPW + 16 * j + lq;
+    const int r = r_first + wrow * RPW + 16 * j + lq;
     qvalid[j] = r <= r_last;
     const int pos = qvalid[j] ? r / G : 0;
     const int g = qvalid[j] ? r - pos * G : 0;
@@ -148,16 +163,16 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
     qlo[j] = a.window > 0 ? max(0, qpos[j] - a.window + 1) : 0;
     const uint16_t* qrow = a.q + (static_cast<size_t>(q0 + pos) * a.hq + kvh * G + g) * D;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qreg[j][ks] = qvalid[j] ? *reinterpret_cast<const uint4*>(qrow + ks * 32 + lg * 8)
+    for (int ks = 0; ks < KSW; ++ks)
+      qreg[j][ks] = qvalid[j] ? *reinterpret_cast<const uint4*>(qrow + (half * KSW + ks) * 32 + lg * 8)
                               : make_uint4(0, 0, 0, 0);
   }
 
-  floatx4_t o[JT][NT];
+  floatx4_t o[JT][NTW];
 #pragma unroll
   for (int j = 0; j < JT; ++j)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) o[j][nt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < NTW; ++nt) o[j][nt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   // Reference max per query row in scaled log2 units (scale > 0, so the max
   // of the raw scores scales to it), and its negation for the exponent.
   float mc[JT], negc[JT];
@@ -310,16 +325,17 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
   // The K fragment reads run PF fragments ahead of the products and the key
   // sub-tiles' accumulation chains alternate; scheduling barriers keep that
   // order (left to itself the compiler waits on each read right before its
-  // product, which a second wave on the SIMD can only partly hide and, at
-  // head_dim 512 with one wave per SIMD, nothing hides).
+  // product, which a second wave on the SIMD can only partly hide). With the
+  // head dimension split, the wave's k-steps start at half * KSW: whole
+  // groups of four, so the half only moves the row base.
   auto tile_s = [&](Scores& sc, const uint16_t* ks_buf) {
-    const uint16_t* krow = ks_buf + lq * D;
+    const uint16_t* krow = ks_buf + lq * D + half * (KSW / 4) * 128;
     auto kfrag = [&](int t4, int ks) {
       const int pos = (((4 * (ks & 3) + lg) ^ swz_k(lq)) << 3) + (ks >> 2) * 128;
       return *reinterpret_cast<const uint4*>(krow + t4 * 16 * D + pos);
     };
     constexpr int PF = 4;
-    constexpr int NR = NS * KS;  // K fragments of one tile; fragment u: sub-tile u % NS, step u / NS
+    constexpr int NR = NS * KSW;  // K fragments of one tile; fragment u: sub-tile u % NS, step u / NS
     uint4 kf[PF + 1];
 #pragma unroll
     for (int t4 = 0; t4 < NS; ++t4)
@@ -402,23 +418,9 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
 #pragma unroll
         for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * lg + i);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+        for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if constexpr (D >= 512) {
-              // The accumulators live in AGPRs (the matrix core's accumulation
-              // registers) at this size; scaling them in place here keeps the
-              // compiler from carrying them through the loop in ordinary
-              // registers and copying all of them across every tile.
-              float x = o[j][nt][i];
-              float t;
-              asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-                           : "+a"(x), "=&v"(t) : "v"(al[i]));
-              o[j][nt][i] = x;
-            } else {
-              o[j][nt][i] *= al[i];
-            }
-          }
+          for (int i = 0; i < 4; ++i) o[j][nt][i] *= al[i];
 #pragma unroll
         for (int i = 0; i < 4; ++i) lsum[j][i] *= al[i];
       }
@@ -448,28 +450,30 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
   // addresses row key0 + j/4, columns 16nt + 4(j%4) .. +3.
   auto tile_pv = [&](const uint16_t* vs_buf) {
     if constexpr (D >= 256) {
-      // The V fragment reads (fragment u: 32-key step u / NT, column tile
-      // u % NT) run PF fragments ahead of the products, as in tile_s; up to
-      // head_dim 128 the compiler's own order measured as fast.
+      // The V fragment reads (fragment u: 32-key step u / NTW, column tile
+      // u % NTW of the wave's part) run PF fragments ahead of the products, as
+      // in tile_s; up to head_dim 128 the compiler's own order measured as
+      // fast. A split wave's column tiles start at half * NTW, whole groups of
+      // eight: the half only moves the base.
       const int vrow = 4 * lg + (lq >> 2);  // + 32 kk, and + 16: same swizzle
-      const uint16_t* vbase = &vs_buf[vrow * D + 4 * (lq & 1)];
+      const uint16_t* vbase = &vs_buf[vrow * D + 4 * (lq & 1)] + half * (NTW / 8) * 128;
       const int vsw = swz_v(vrow);
       auto vfrag = [&](int u) {
-        const int kk = u / NT, nt = u % NT;
+        const int kk = u / NTW, nt = u % NTW;
         const int vc = (((2 * (nt & 7) + ((lq & 3) >> 1)) ^ vsw) << 3) + (nt >> 3) * 128 + kk * 32 * D;
         const uint2 v0 = ds_read_tr16(vbase + vc);
         const uint2 v1 = ds_read_tr16(vbase + 16 * D + vc);
         return make_uint4(v0.x, v0.y, v1.x, v1.y);
       };
       constexpr int PF = 4;
-      constexpr int NV = NK * NT;
+      constexpr int NV = NK * NTW;
       uint4 vf[PF + 1];
 #pragma unroll
       for (int u = 0; u < PF; ++u) vf[u] = vfrag(u);
 #pragma unroll
       for (int u = 0; u < NV; ++u) {
         if (u + PF < NV) vf[(u + PF) % (PF + 1)] = vfrag(u + PF);
-        const int kk = u / NT, nt = u % NT;
+        const int kk = u / NTW, nt = u % NTW;
         if (nt == 0) {
 #pragma unroll
           for (int j = 0; j < JT; ++j) lsum[j] = mfma16x16x32(pa[j][kk], ones, lsum[j]);
@@ -487,7 +491,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
         const uint16_t* vbase = &vs_buf[vrow * D + 4 * (lq & 1)];
         const int vsw = swz_v(vrow);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
+        for (int nt = 0; nt < NTW; ++nt) {
           // Chunk 2nt + b = 16 (nt / 8) + (2 (nt % 8) + b); the swizzle (below 16)
           // touches only the second part.
           const int vc = (((2 * (nt & 7) + ((lq & 3) >> 1)) ^ vsw) << 3) + (nt >> 3) * 128;
@@ -527,6 +531,25 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
     __builtin_amdgcn_s_setprio(1);
     tile_s(sc, k_s[buf]);
     __builtin_amdgcn_s_setprio(0);
+    if constexpr (SPL > 1) {
+      // The partner wave (same rows, other half of head_dim) holds the rest
+      // of each score: exchange through LDS and add. Both waves add the same
+      // two values, so both hold bit-identical scores (and probabilities).
+#pragma unroll
+      for (int j = 0; j < JT; ++j)
+#pragma unroll
+        for (int t4 = 0; t4 < NS; ++t4) exch[wave][j * NS + t4][lane] = sc[j][t4];
+      __syncthreads();
+      const int partner = wave ^ RG;
+#pragma unroll
+      for (int j = 0; j < JT; ++j)
+#pragma unroll
+        for (int t4 = 0; t4 < NS; ++t4) {
+          const floatx4_t other = exch[partner][j * NS + t4][lane];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sc[j][t4][i] += other[i];
+        }
+    }
     tile_softmax(sc, needs_mask(ts) || absent != 0, ts, absent);
     // FP8 codes up to head_dim 128 are widened into the other buffer before
     // the P.V part, so the LDS stores drain under it rather than before the
@@ -548,14 +571,14 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
     for (int i = 0; i < 4; ++i) inv[i] = lsum[j][i] > 0.f ? a.v_scale / lsum[j][i] : 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = r_first + wave * RPW + 16 * j + 4 * lg + i;
+      const int r = r_first + wrow * RPW + 16 * j + 4 * lg + i;
       if (r > r_last) continue;
       const int pos = r / G;
       const int g = r - pos * G;
       uint16_t* orow = a.out + (static_cast<size_t>(q0 + pos) * a.hq + kvh * G + g) * D;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        orow[nt * 16 + lq] = static_cast<uint16_t>(f32_to_bf16_bits(o[j][nt][i] * inv[i]));
+      for (int nt = 0; nt < NTW; ++nt)
+        orow[(half * NTW + nt) * 16 + lq] = static_cast<uint16_t>(f32_to_bf16_bits(o[j][nt][i] * inv[i]));
     }
   }
 }
@@ -617,7 +640,7 @@ int32_t prefill_impl(void* out, const void* q, const void* k_pool, const void* v
   if (batch == 0 || total_q == 0 || max_q_len == 0) return ok();
   const int group = num_q_heads / num_kv_heads;
   const int nw = (waves == 4 || waves == 8) && head_dim < 256 ? waves : default_waves(head_dim);
-  const int tm = nw * rows_per_wave(head_dim);
+  const int tm = nw / splits(head_dim) * rows_per_wave(head_dim);
   const int64_t tiles = (static_cast<int64_t>(max_q_len) * group + tm - 1) / tm;
   const int64_t items = tiles * num_kv_heads * batch;
   if (items > (1LL << 30)) return fail(PAGED_ERR_INVALID_ARG, "problem too large");
@@ -649,8 +672,8 @@ int32_t prefill_impl(void* out, const void* q, const void* k_pool, const void* v
     hipExtLaunchKernelGGL(kern, grid, block, 0, s, tr.start(), tr.stop(), 0, prm);
   };
   if (head_dim == 512) {
-    if (esz == 1) launch(prefill_kernel<512, 1, 4>);
-    else launch(prefill_kernel<512, 2, 4>);
+    if (esz == 1) launch(prefill_kernel<512, 1, 8>);
+    else launch(prefill_kernel<512, 2, 8>);
   } else if (head_dim == 256) {
     if (esz == 1) launch(prefill_kernel<256, 1, 8>);
     else launch(prefill_kernel<256, 2, 8>);
