@@ -788,38 +788,52 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_lds_kernel(D
       if (lg == 0 && lq >= g0 && lq < g1) my_ml[(lq - g0) * 2] = mc;
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < (g1 - g0) * D; idx += blockDim.x) {
-      const int gl = idx / D;
+    // Four consecutive columns per thread and step: 16-byte LDS reads, one
+    // weight computation per four outputs, 8-byte (bf16) or 16-byte (partial)
+    // stores. With one wave per SIMD nothing hides per-instruction cost, so
+    // the instruction count of this loop is the merge's time.
+    constexpr int QD = D / 4;  // column quads per row
+    for (int v = threadIdx.x; v < (g1 - g0) * QD; v += blockDim.x) {
+      const int gl = v / QD;
       const int g = g0 + gl;
-      const int d = idx - gl * D;
+      const int d = (v - gl * QD) * 4;
       // Every wave slot is read at once (all lie inside the rings); the entries
       // of waves past nw, which did not run, are then ignored.
-      float mw[kDecodeWaves], lw[kDecodeWaves], ow[kDecodeWaves];
+      float mw[kDecodeWaves], lw[kDecodeWaves];
+      floatx4_t ow[kDecodeWaves];
 #pragma unroll
       for (int w = 0; w < kDecodeWaves; ++w) {
         const float2 ml = *reinterpret_cast<const float2*>(sm_ml + w * kML + gl * 2);
         mw[w] = ml.x;
         lw[w] = ml.y;
-        ow[w] = sm_o[w * kO + gl * D + d];
+        ow[w] = *reinterpret_cast<const floatx4_t*>(sm_o + w * kO + gl * D + d);
       }
       float M = kNegInf;
 #pragma unroll
       for (int w = 0; w < kDecodeWaves; ++w) M = w < nw ? fmaxf(M, mw[w]) : M;
-      float L = 0.f, A = 0.f;
+      float L = 0.f;
+      floatx4_t A = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int w = 0; w < kDecodeWaves; ++w) {
         const bool live = w < nw && mw[w] != kNegInf;
         const float f = live ? fast_exp2(mw[w] - M) : 0.f;
         L = live ? fmaf(lw[w], f, L) : L;
-        A = live ? fmaf(ow[w], f, A) : A;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) A[e] = live ? fmaf(ow[w][e], f, A[e]) : A[e];
       }
       const size_t bh = static_cast<size_t>(b) * a.hq + h0 + g;
-      A *= a.v_scale;  // FP8: V codes stand for v_scale * value (1 for bf16: exact)
       if (a.out) {
-        store_out<2>(a.out, bh * D + d, L > 0.f ? A / L : 0.f);
+        // FP8: V codes stand for v_scale * value (1 for bf16: exact)
+        const float s = L > 0.f ? a.v_scale / L : 0.f;
+        uint2 pk;
+        pk.x = pack_bf16x2(A[0] * s, A[1] * s);
+        pk.y = pack_bf16x2(A[2] * s, A[3] * s);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + bh * D + d) = pk;
       } else {
         const size_t slot = bh * a.max_parts + p;
-        a.ws_acc[slot * D + d] = A;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) A[e] *= a.v_scale;
+        *reinterpret_cast<floatx4_t*>(a.ws_acc + slot * D + d) = A;
         if (d == 0) {
           a.ws_ml[slot * 2] = M;
           a.ws_ml[slot * 2 + 1] = L;
