@@ -25,12 +25,15 @@ one HIP graph. ``cpu_baseline`` times the float64 oracle on a bounded sample.
 
     python bench.py [--workload headline|qwen3|mixed|hybrid|prefill|hprefill|mixedstep|tiny]
                     [--kv bf16|fp8] [--head-dim D] [--partition-tokens P] [--warm]
-                    [--steps K] [--warmup W]
+                    [--shard N] [--steps K] [--warmup W]
 
 ``--kv fp8`` runs the same workload over FP8 (E4M3) pools with per-layer
 scales (quantizing write, FP8 decode/prefill); the decode byte count then
 counts one byte per K/V element. ``--head-dim`` changes the workload's head
 dimension (e.g. 512 for the Gemma-style hybrid decode or prefill).
+``--shard N`` times one GPU's share of an N-GPU run of the workload (its KV
+heads split N ways when they divide, else its rows) on this one GPU; the line
+then reports that GPU's throughput on its share.
 """
 
 from __future__ import annotations
@@ -378,6 +381,27 @@ def roofline_entry(kernels, durations, steps, work_per_step, bound, traffic=None
     return e
 
 
+# (rows, query heads, KV heads) of each workload at its full size.
+FULL_SHAPES = {"tiny": (2, 4, 2), "qwen3": (4, 16, 8), "mixed": (32, 32, 8), "hybrid": (8, 8, 1),
+               "prefill": (1, 32, 8), "hprefill": (4, 8, 1), "mixedstep": (32, 32, 8)}
+
+
+def shard_overrides(name, n):
+    """Shape overrides for one GPU's share of an n-GPU run, and how it splits:
+    the KV heads n ways when they divide (each GPU holds Hkv/n heads of every
+    pool and the matching query heads; nothing is exchanged inside attention),
+    else the rows (each GPU owns its requests' pools and tables)."""
+    if n <= 1:
+        return {}, None
+    B, hq, hkv = FULL_SHAPES[name]
+    if hkv % n == 0:
+        return {"hq": hq // n, "hkv": hkv // n}, "kv_heads"
+    if B % n == 0:
+        return {"batch": B // n}, "rows"
+    print(f"bench.py: {name} splits neither its {hkv} KV heads nor its {B} rows {n} ways", file=sys.stderr)
+    sys.exit(2)
+
+
 def run_part(pk, args, name, steps, warmup):
     """Build workload ``name``, time its steps (graph) and its kernels (eager,
     scrubbed and warm); return the fields of a bench line for it."""
@@ -398,6 +422,8 @@ def run_part(pk, args, name, steps, warmup):
         kw["head_dim"] = args.head_dim
     if args.partition_tokens is not None:
         kw["part"] = args.partition_tokens
+    shard_kw, shard_split = shard_overrides(name, args.shard)
+    kw.update(shard_kw)
     log(f"[bench] building workload {name} ({kw})")
     wl = synth.make(name, **kw)
     R = waves if name == "qwen3" else 1
@@ -418,6 +444,9 @@ def run_part(pk, args, name, steps, warmup):
     else:
         outs = {L.name: torch.empty_like(dev[L.name]["q"]) for L in wl.layers}
     ws = runner.gpu_workspace(_subset(wl, list(range(wsz))) if R > 1 else wl, dev)
+    # The prefill's key-split workspace (None when the library does not split
+    # these shapes on this device: query tiles enough to fill it).
+    pws = runner.prefill_workspace(wl) if wl.kind == "prefill" and not mixed_step else None
     for r in range(R):
         rows = slice(r * wsz, (r + 1) * wsz)
         seq = []
@@ -460,12 +489,12 @@ def run_part(pk, args, name, steps, warmup):
                 seq.append(pk.paged_attn_prefill_chunk_fp8(
                     outs[L.name], d["q"], d["k_pool"], d["v_pool"], d["tables"], dev["_cu_q"],
                     dev["_seq_lens"], int(wl.chunk_lens.max()), wl.scale, L.k_scale, L.v_scale,
-                    sliding_window=L.window, stream=stream, prepare=True))
+                    sliding_window=L.window, workspace=pws, stream=stream, prepare=True))
             else:
                 seq.append(pk.paged_attn_prefill_chunk(
                     outs[L.name], d["q"], d["k_pool"], d["v_pool"], d["tables"], dev["_cu_q"],
                     dev["_seq_lens"], int(wl.chunk_lens.max()), wl.scale, sliding_window=L.window,
-                    stream=stream, prepare=True))
+                    workspace=pws, stream=stream, prepare=True))
         calls.append(seq)
 
     def step(i):
@@ -521,7 +550,8 @@ def run_part(pk, args, name, steps, warmup):
     dur_warm = dur_cold if args.warm else timed_pass(pk, stream, calls, warmup, ksteps, n_writes, scrub=False)
     caches = "warm (back to back)" if args.warm else "scrubbed (1 GiB read before each attention launch)"
 
-    tag = name + (f"_d{args.head_dim}" if args.head_dim else "") + ("_fp8" if fp8 else "")
+    tag = (name + (f"_d{args.head_dim}" if args.head_dim else "") + ("_fp8" if fp8 else "")
+           + (f"_shard{args.shard}" if shard_split else ""))
     nl = len(wl.layers)
     part = {"name": name, "wl": wl, "tabs": tabs, "ms_per_step": ms_per_step, "timing": timing,
             "ksteps": ksteps, "caches": caches}
@@ -566,9 +596,11 @@ def run_part(pk, args, name, steps, warmup):
     else:
         work = prefill_flops(wl)
         part["value"], part["unit"] = work / (ms_per_step * 1e-3) / 1e12, "TFLOP/s"
-        part["roofline"] = roofline_entry(["prefill"], dur_cold, ksteps, work, "mfma",
-                                          counter_traffic_step({"prefill": nl}, tag), {"traffic_per": "step"})
-        part["roofline_warm"] = roofline_entry(["prefill"], dur_warm, ksteps, work, "mfma")
+        # With a key split the prefill's time is its two kernels together.
+        pk_names = ["prefill", "prefill_reduce"] if dur_cold.get("prefill_reduce") else ["prefill"]
+        traffic = counter_traffic_step({"prefill": nl}, tag) if len(pk_names) == 1 else None
+        part["roofline"] = roofline_entry(pk_names, dur_cold, ksteps, work, "mfma", traffic, {"traffic_per": "step"})
+        part["roofline_warm"] = roofline_entry(pk_names, dur_warm, ksteps, work, "mfma")
         if nl > 1:
             dd = dur_cold.get("prefill", [])
             extra["kernel_us_by_layer"] = {"prefill": {L.name: round(float(np.mean(dd[i::nl])) * 1e3, 3)
@@ -584,6 +616,8 @@ def run_part(pk, args, name, steps, warmup):
         "pool_blocks": [L.num_blocks for L in wl.layers if not L.alias_of],
         "kv_dtype": "fp8_e4m3" if fp8 else wl.dtype,
     }
+    if shard_split:
+        part["config"]["shard"] = {"of_gpus": args.shard, "split": shard_split}
     if mixed_step:
         part["config"]["decode_rows"] = wl.num_decode
         part["config"]["chunk_tokens"] = [int(c) for c in wl.chunk_lens[wl.num_decode:]]
@@ -606,6 +640,8 @@ def main():
     ap.add_argument("--head-dim", type=int, default=None, help="head_dim override (e.g. 512 for the hybrid decode)")
     ap.add_argument("--partition-tokens", type=int, default=None,
                     help="decode split-K partition size (default: the workload's, else the library rule)")
+    ap.add_argument("--shard", type=int, default=1,
+                    help="time one GPU's share of an N-GPU run (KV heads split N ways when they divide, else rows)")
     ap.add_argument("--warm", action="store_true",
                     help="time kernels back to back only (no 1 GiB read before each attention launch)")
     ap.add_argument("--scrub", action="store_true", help="(default; kept for older command lines)")

@@ -38,6 +38,7 @@ KERNELS = {
     "decode_partial": 2,
     "decode_reduce": 3,
     "prefill": 4,
+    "prefill_reduce": 5,
 }
 
 _c_int32 = ctypes.c_int32
@@ -68,7 +69,8 @@ _SIGNATURES = {
     "paged_attn_decode_fp8": [_c_void_p] * 5 + [_c_int32, _c_void_p] + [_c_int32] * 6 + [_c_float] * 3
     + [_c_int32] * 3 + [_c_void_p, _c_size, _c_void_p],
     "paged_attn_prefill_chunk_fp8": [_c_void_p] * 5 + [_c_int32, _c_void_p, _c_void_p] + [_c_int32] * 8
-    + [_c_float] * 3 + [_c_int32, _c_void_p],
+    + [_c_float] * 3 + [_c_int32, _c_void_p, _c_size, _c_void_p],
+    "paged_attn_prefill_chunk_workspace_bytes": [_c_int32] * 6 + [ctypes.POINTER(_c_size)],
     "paged_attn_mixed": [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int32, _c_void_p,
                          _c_void_p, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
                          _c_int32, _c_int32, _c_int32, _c_float, _c_float, _c_float, _c_int32,
@@ -80,7 +82,7 @@ _SIGNATURES = {
     "paged_attn_decode_noalloc": [_c_void_p] * 5 + [_c_int32, _c_void_p] + [_c_int32] * 6 + [_c_float]
     + [_c_int32] * 4 + [_c_void_p],
     "paged_attn_prefill_chunk": [_c_void_p] * 5 + [_c_int32, _c_void_p, _c_void_p] + [_c_int32] * 8
-    + [_c_float, _c_int32, _c_int32, _c_void_p],
+    + [_c_float, _c_int32, _c_void_p, _c_size, _c_int32, _c_void_p],
     "paged_trace_enable": [_c_int32],
     "paged_trace_reset": [],
     "paged_trace_query": [_c_int32, ctypes.POINTER(ctypes.c_double), _P_I64],
@@ -304,9 +306,27 @@ def paged_attn_decode_noalloc(out, q, k_pool, v_pool, block_tables, seq_lens, sc
         prepare)
 
 
+def paged_attn_prefill_chunk_workspace_bytes(batch, total_q, max_q_len, num_q_heads, num_kv_heads,
+                                             head_dim):
+    """Workspace bytes of the prefill's key split for these shapes (0: none)."""
+    out = _c_size()
+    _check(lib.paged_attn_prefill_chunk_workspace_bytes(batch, total_q, max_q_len, num_q_heads,
+                                                        num_kv_heads, head_dim, ctypes.byref(out)))
+    return out.value
+
+
+def _workspace(workspace):
+    if workspace is None:
+        return None, 0
+    return _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+
+
 def paged_attn_prefill_chunk(out, q, k_pool, v_pool, block_tables, cu_q_lens, seq_lens, max_q_len,
-                             scale, sliding_window=0, stream=None, prepare=False):
-    """Chunked prefill: ``out, q [T, Hq, D]`` bf16; ``cu_q_lens [B+1]``, ``seq_lens [B]`` int32."""
+                             scale, sliding_window=0, workspace=None, stream=None, prepare=False):
+    """Chunked prefill: ``out, q [T, Hq, D]`` bf16; ``cu_q_lens [B+1]``, ``seq_lens [B]`` int32.
+
+    ``workspace``: None (no key split), or a uint8 device tensor of at least
+    ``paged_attn_prefill_chunk_workspace_bytes(...)`` bytes."""
     torch = _torch()
     nb, hkv, bs, d = _pool_geom(k_pool, v_pool)
     T, hq, dq = (int(x) for x in q.shape)
@@ -320,7 +340,7 @@ def paged_attn_prefill_chunk(out, q, k_pool, v_pool, block_tables, cu_q_lens, se
         _dev(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
         _dev(cu_q_lens, "cu_q_lens", torch.int32, 1), _dev(seq_lens, "seq_lens", torch.int32, 1),
         B, T, int(max_q_len), hq, hkv, d, bs, nb, float(scale), int(sliding_window),
-        _dtype_code(q), _stream(stream)), prepare)
+        *_workspace(workspace), _dtype_code(q), _stream(stream)), prepare)
 
 
 def paged_attn_mixed(out, q, k_pool, v_pool, block_tables, cu_q_lens, seq_lens, num_decode_rows,
@@ -397,8 +417,8 @@ def paged_attn_decode_fp8(out, q, k_pool, v_pool, block_tables, seq_lens, scale,
 
 
 def paged_attn_prefill_chunk_fp8(out, q, k_pool, v_pool, block_tables, cu_q_lens, seq_lens,
-                                 max_q_len, scale, k_scale, v_scale, sliding_window=0, stream=None,
-                                 prepare=False):
+                                 max_q_len, scale, k_scale, v_scale, sliding_window=0, workspace=None,
+                                 stream=None, prepare=False):
     """Chunked prefill over float8_e4m3fn pools; ``out, q [T, Hq, D]`` bf16."""
     torch = _torch()
     nb, hkv, bs, d = _fp8_pools(k_pool, v_pool)
@@ -413,7 +433,7 @@ def paged_attn_prefill_chunk_fp8(out, q, k_pool, v_pool, block_tables, cu_q_lens
         _dev(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
         _dev(cu_q_lens, "cu_q_lens", torch.int32, 1), _dev(seq_lens, "seq_lens", torch.int32, 1),
         B, T, int(max_q_len), hq, hkv, d, bs, nb, float(scale), float(k_scale), float(v_scale),
-        int(sliding_window), _stream(stream)), prepare)
+        int(sliding_window), *_workspace(workspace), _stream(stream)), prepare)
 
 
 # ------------------------------------------------------------------ tracing

@@ -29,14 +29,16 @@ int32_t decode_check(const void* out, const void* q, const void* k_pool, const v
 // Chunked prefill over pools of esz-byte elements (2 bf16, 1 FP8 codes); q and
 // out bf16. cu_q_lens holds absolute offsets into q and out. waves: 4 or 8
 // waves per workgroup up to head_dim 128 (head_dim 256 and 512 take 8
-// whatever is asked), 0 for the default.
+// whatever is asked), 0 for the default. workspace NULL: no key split; else
+// the key split of the library rule, its partials in the workspace.
 int32_t prefill_impl(void* out, const void* q, const void* k_pool, const void* v_pool,
                      const int32_t* block_tables, int32_t max_blocks_per_seq,
                      const int32_t* cu_q_lens, const int32_t* seq_lens, int32_t batch,
                      int32_t total_q, int32_t max_q_len, int32_t num_q_heads,
                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                      int32_t num_blocks, float scale, float k_scale, float v_scale,
-                     int32_t sliding_window, int esz, void* stream, int waves = 0);
+                     int32_t sliding_window, void* workspace, size_t workspace_bytes, int esz,
+                     void* stream, int waves = 0);
 
 // Every argument check of prefill_impl, with nothing enqueued.
 int32_t prefill_check(const void* out, const void* q, const void* k_pool, const void* v_pool,

@@ -935,6 +935,91 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeParams a) {
     store_out<ESZ>(a.out, static_cast<size_t>(pair) * D + c0l + 64 * WPP * k, o[k] * inv);
 }
 
+// Rows with more partitions than one chunk of the kernel above holds (64,
+// or 32 at head_dim 512): a workgroup per (row, query head, 64 columns), lane
+// l owning one column; its four waves take chunks of 64 partitions w, w + 4,
+// ... (every wave's first chunk requested before the row length is known),
+// each combines its chunks with an online maximum, and the four results are
+// combined through LDS. Up to 256 partitions (C4's 32768-token rows at one row
+// per GPU) this is one round trip to memory instead of one per chunk.
+template <int ESZ, int D>
+__global__ __launch_bounds__(256) void decode_reduce_wide_kernel(DecodeParams a) {
+  constexpr float kNegInf = -INFINITY;
+  constexpr int kSlices = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int pair = blockIdx.x / kSlices;
+  const int col = (blockIdx.x - pair * kSlices) * 64 + lane;
+  const int b = pair / a.hq;
+  const int P = a.max_parts;
+  const float* ml = a.ws_ml + static_cast<size_t>(pair) * P * 2;
+  const float* acc = a.ws_acc + static_cast<size_t>(pair) * P * D;
+  const int nch = (P + 63) / 64;
+
+  float2 mlc = make_float2(kNegInf, 0.f);
+  float x[64];
+  auto load = [&](int c) {
+    const int p0 = c * 64;
+    mlc = p0 + lane < P ? *reinterpret_cast<const float2*>(ml + 2 * static_cast<size_t>(p0 + lane))
+                        : make_float2(kNegInf, 0.f);
+#pragma unroll
+    for (int u = 0; u < 64; ++u) x[u] = p0 + u < P ? acc[static_cast<size_t>(p0 + u) * D + col] : 0.f;
+  };
+  if (wave < nch) load(wave);
+
+  const int n = a.seq_lens[b];
+  const int lo = a.window > 0 ? max(0, n - a.window) : 0;
+  const int s0 = (lo >> a.bs_log2) << a.bs_log2;
+  const int np = n > s0 ? min((n - s0 + a.part - 1) / a.part, P) : 0;
+
+  float M = kNegInf, L = 0.f, o = 0.f;
+  for (int c = wave; c < nch && c * 64 < np; c += 4) {
+    if (c != wave) load(c);
+    const bool live = c * 64 + lane < np;
+    const float mp = live ? mlc.x : kNegInf;
+    const float lp = live ? mlc.y : 0.f;
+    float cm = mp;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) cm = fmaxf(cm, __shfl_xor(cm, off));
+    const float newM = fmaxf(M, cm);
+    const float f = M == kNegInf ? 0.f : fast_exp2(M - newM);
+    const float w = mp == kNegInf ? 0.f : fast_exp2(mp - newM);
+    float lw = lp * w;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) lw += __shfl_xor(lw, off);
+    L = L * f + lw;
+    o *= f;
+#pragma unroll
+    for (int u = 0; u < 64; ++u) {
+      // partition c*64 + u: weight held by lane u (zero past np)
+      const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u));
+      o = fmaf(c * 64 + u < np ? x[u] : 0.f, wu, o);
+    }
+    M = newM;
+  }
+
+  __shared__ float sm_m[4], sm_l[4], sm_o[4][64];
+  if (lane == 0) {
+    sm_m[wave] = M;
+    sm_l[wave] = L;
+  }
+  sm_o[wave][lane] = o;
+  __syncthreads();
+  if (wave != 0) return;
+  float MM = kNegInf;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) MM = fmaxf(MM, sm_m[w]);
+  float LL = 0.f, OO = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float mw = sm_m[w];
+    const float f = mw == kNegInf ? 0.f : fast_exp2(mw - MM);
+    LL = fmaf(sm_l[w], f, LL);
+    OO = fmaf(sm_o[w][lane], f, OO);
+  }
+  store_out<ESZ>(a.out, static_cast<size_t>(pair) * D + col, LL > 0.f ? OO / LL : 0.f);
+}
+
 // Tokens one wave of the fp32 kernel processes per iteration.
 int iter_tokens_f32(int d) {
   return d == 64 ? Geo<4, 64>::ITER : d == 128 ? Geo<4, 128>::ITER : Geo<4, 256>::ITER;
@@ -1073,13 +1158,14 @@ void launch_partial_any(const DecodeParams& prm, int kv_esz, int d, int gt, dim3
 
 // Waves per (row, query head) for the reduce: the fewest for which the
 // pair's partitions (up to 64) fit one chunk of 64 / columns-per-lane.
+// Waves per (row, query head) of decode_reduce_kernel: the fewest for which a
+// row's partitions fit one chunk; 0 when none does (decode_reduce_wide_kernel).
 int reduce_waves_per_pair(int d, int max_parts) {
-  const int p = std::min(max_parts, 64);
   for (int wpp = 1; wpp <= 4; wpp *= 2) {
     const int cpt = d / (64 * wpp);
-    if (cpt >= 1 && cpt * p <= 64) return wpp;
+    if (cpt >= 1 && cpt * max_parts <= 64) return wpp;
   }
-  return d >= 256 ? 4 : d / 64;
+  return 0;
 }
 
 template <int ESZ, int D>
@@ -1106,9 +1192,23 @@ void launch_reduce_w(const DecodeParams& prm, int wpp, hipStream_t s, const Laun
   }
 }
 
+template <int ESZ, int D>
+void launch_reduce_wide(const DecodeParams& prm, hipStream_t s, const LaunchTrace& tr) {
+  const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(prm.batch) * prm.hq * (D / 64)));
+  hipExtLaunchKernelGGL(decode_reduce_wide_kernel<ESZ, D>, grid, dim3(256), 0, s, tr.start(), tr.stop(), 0,
+                        prm);
+}
+
 template <int ESZ>
 void launch_reduce_d(const DecodeParams& prm, int d, hipStream_t s, const LaunchTrace& tr) {
   const int wpp = reduce_waves_per_pair(d, prm.max_parts);
+  if (wpp == 0) {
+    if (d == 64) launch_reduce_wide<ESZ, 64>(prm, s, tr);
+    else if (d == 128) launch_reduce_wide<ESZ, 128>(prm, s, tr);
+    else if (d == 256) launch_reduce_wide<ESZ, 256>(prm, s, tr);
+    else if constexpr (ESZ == 2) launch_reduce_wide<ESZ, 512>(prm, s, tr);
+    return;
+  }
   if (d == 64) launch_reduce_w<ESZ, 64>(prm, wpp, s, tr);
   else if (d == 128) launch_reduce_w<ESZ, 128>(prm, wpp, s, tr);
   else if (d == 256) launch_reduce_w<ESZ, 256>(prm, wpp, s, tr);
@@ -1175,6 +1275,8 @@ int32_t decode_check_plan(const void* out, const void* q, const void* k_pool, co
     return fail(PAGED_ERR_INVALID_ARG, "k_scale and v_scale must be finite and positive");
   if (batch > 65535 || num_q_heads > 65535)
     return fail(PAGED_ERR_INVALID_ARG, "batch and num_q_heads must be at most 65535");
+  if (static_cast<int64_t>(batch) * num_q_heads > (1 << 24))
+    return fail(PAGED_ERR_INVALID_ARG, "batch * num_q_heads must be at most 2^24");
   if (pl->max_parts > 65535)
     return fail(PAGED_ERR_INVALID_ARG,
                 "max_seq_len %d needs %d partitions of %d tokens; at most 65535 are supported",

@@ -45,7 +45,8 @@ extern "C" int32_t paged_attn_mixed(void* out, const void* q, const void* k_pool
   if (nd == 0)
     return prefill_impl(out, q, k_pool, v_pool, block_tables, max_blocks_per_seq, cu_q_lens,
                         seq_lens, np, total_q, max_q_len, num_q_heads, num_kv_heads, head_dim,
-                        block_size, num_blocks, scale, k_scale, v_scale, sliding_window, esz, stream);
+                        block_size, num_blocks, scale, k_scale, v_scale, sliding_window, nullptr, 0,
+                        esz, stream);
 
   // Both parts: check everything either could reject before enqueuing anything.
   if (int32_t rc = prefill_check(out, q, k_pool, v_pool,
@@ -73,7 +74,8 @@ extern "C" int32_t paged_attn_mixed(void* out, const void* q, const void* k_pool
   int32_t rc = prefill_impl(out, q, k_pool, v_pool, block_tables + static_cast<size_t>(nd) * max_blocks_per_seq,
                             max_blocks_per_seq, cu_q_lens + nd, seq_lens + nd, np, total_q - nd,
                             max_q_len, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                            scale, k_scale, v_scale, sliding_window, esz, side.get(), /*waves=*/4);
+                            scale, k_scale, v_scale, sliding_window, /*workspace=*/nullptr, 0, esz,
+                            side.get(), /*waves=*/4);
   if (rc == PAGED_OK)
     rc = decode_impl(out, q, k_pool, v_pool, block_tables, max_blocks_per_seq, seq_lens, nd,
                      num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, k_scale,

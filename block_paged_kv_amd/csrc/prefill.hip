@@ -71,10 +71,17 @@ struct PrefillParams {
   const int32_t* seq_lens;
   int32_t mb, hq, hkv, group, bs_log2, nb, window;
   int32_t tiles_per_head;   // ceil(max_q_len * group / query rows per workgroup)
-  int32_t work_items;       // batch * hkv * tiles_per_head
+  int32_t ksplit;           // key ranges per query tile (1: the whole range, output directly)
+  int32_t work_items;       // batch * hkv * ksplit * tiles_per_head
   int32_t per_xcd;          // ceil(work_items / kNumXcd)
+  int32_t total_q;
   float scale_log2;         // scale * log2(e) (times the K scale for FP8 pools)
   float v_scale;            // FP8 pools: the V scale; 1 otherwise
+  // ksplit > 1: per key range s, query token t, query head h the unnormalised
+  // output (times v_scale) at ws_acc[((s * total_q + t) * hq + h) * D] and
+  // (reference max in scaled log2 units, probability sum) at ws_ml[... * 2].
+  float* ws_acc;
+  float* ws_ml;
 };
 
 __device__ __forceinline__ floatx4_t mfma16x16x32(const uint4& a, const uint4& b, floatx4_t c) {
@@ -123,9 +130,13 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
   const int lin = blockIdx.x;
   const int item = (lin % kNumXcd) * a.per_xcd + lin / kNumXcd;
   if (item >= a.work_items) return;
+  // Query tile fastest, then key range: consecutive items (one XCD) read the
+  // same keys of one KV head.
   const int tile = item % a.tiles_per_head;
-  const int kvh = (item / a.tiles_per_head) % a.hkv;
-  const int b = item / (a.tiles_per_head * a.hkv);
+  const int rest = item / a.tiles_per_head;
+  const int ksp = rest % a.ksplit;
+  const int kvh = (rest / a.ksplit) % a.hkv;
+  const int b = rest / (a.ksplit * a.hkv);
 
   const int q0 = a.cu_q[b];
   const int C = a.cu_q[b + 1] - q0;
@@ -190,8 +201,16 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
   const int32_t* bt = a.bt + static_cast<size_t>(b) * a.mb;
   const int bs_log2 = a.bs_log2;
   const int bs_mask = (1 << bs_log2) - 1;
-  const int kt_begin = lo_min / kTileN;
-  const int kt_end = a_max / kTileN;  // inclusive
+  // Key tiles of the workgroup's rows; with a key split, range ksp of ksplit
+  // near-equal ranges of them (possibly empty: the partials then say so).
+  int kt_begin = lo_min / kTileN;
+  int kt_end = a_max / kTileN;  // inclusive
+  if (a.ksplit > 1) {
+    const int nkt = kt_end - kt_begin + 1;
+    const int k0 = kt_begin + nkt * ksp / a.ksplit;
+    kt_end = kt_begin + nkt * (ksp + 1) / a.ksplit - 1;
+    kt_begin = k0;
+  }
   // Blocks a K/V tile touches: a 32-key tile lies inside one 64-key block.
   const int tile_blocks = max(1, kTileN >> bs_log2);
   const float c = a.scale_log2;
@@ -509,6 +528,9 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
   // starts before the last row's window start.
   auto needs_mask = [&](int ts) { return (ts + kTileN - 1 > a_min) || (ts < lo_max); };
 
+  // An empty key range (key split only) leaves the row state as it starts:
+  // no keys, weight zero in the reduce.
+  if (kt_begin <= kt_end) {
   int ent_next = load_entries(kt_begin + 1);
   uint64_t absent_next = stage_load(kt_begin, load_entries(kt_begin), 0);
   stage_store(0);
@@ -562,6 +584,29 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
     if (!kEarlyStore && has_next) stage_store(buf ^ 1);
     __syncthreads();
   }
+  }
+
+  if (a.ksplit > 1) {
+    // ---- partials of this key range (the reduce normalises) ------------------
+#pragma unroll
+    for (int j = 0; j < JT; ++j) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // Row 16j + 4lg + i's reference max sits in the S^T layout at lane 4lg + i.
+        const float m = __shfl(mc[j], 4 * lg + i);
+        const int r = r_first + wrow * RPW + 16 * j + 4 * lg + i;
+        if (r > r_last) continue;
+        const int pos = r / G;
+        const int g = r - pos * G;
+        const size_t pr = (static_cast<size_t>(ksp) * a.total_q + q0 + pos) * a.hq + kvh * G + g;
+        float* acc = a.ws_acc + pr * D;
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) acc[(half * NTW + nt) * 16 + lq] = o[j][nt][i] * a.v_scale;
+        if (lq == 0 && half == 0) *reinterpret_cast<float2*>(a.ws_ml + pr * 2) = make_float2(m, lsum[j][i]);
+      }
+    }
+    return;
+  }
 
   // ---- normalise and store --------------------------------------------------
 #pragma unroll
@@ -581,6 +626,48 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
         orow[(half * NTW + nt) * 16 + lq] = static_cast<uint16_t>(f32_to_bf16_bits(o[j][nt][i] * inv[i]));
     }
   }
+}
+
+// Key-split prefill: combine the ksplit partials of each (query token, query
+// head). One wave per pair, lane l holding columns l + 64 k; every partial is
+// requested before any is used (one round trip), ksplit <= kMaxKeySplit.
+constexpr int kMaxKeySplit = 16;
+
+template <int D>
+__global__ __launch_bounds__(256) void prefill_reduce_kernel(PrefillParams a) {
+  constexpr int CPT = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const size_t pairs = static_cast<size_t>(a.total_q) * a.hq;
+  if (pair >= pairs) return;
+  const int S = a.ksplit;
+  float2 ml[kMaxKeySplit];
+  float x[kMaxKeySplit][CPT];
+#pragma unroll
+  for (int s = 0; s < kMaxKeySplit; ++s) {
+    const size_t pr = s * pairs + pair;
+    ml[s] = s < S ? *reinterpret_cast<const float2*>(a.ws_ml + pr * 2) : make_float2(-INFINITY, 0.f);
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) x[s][k] = s < S ? a.ws_acc[pr * D + lane + 64 * k] : 0.f;
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < kMaxKeySplit; ++s) M = fmaxf(M, ml[s].x);
+  float L = 0.f, o[CPT];
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) o[k] = 0.f;
+#pragma unroll
+  for (int s = 0; s < kMaxKeySplit; ++s) {
+    // A range that saw no key of the row (reference max -inf) weighs zero.
+    const float w = ml[s].x == -INFINITY ? 0.f : fast_exp2(ml[s].x - M);
+    L = fmaf(ml[s].y, w, L);
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) o[k] = w != 0.f ? fmaf(x[s][k], w, o[k]) : o[k];
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+  for (int k = 0; k < CPT; ++k)
+    a.out[static_cast<size_t>(pair) * D + lane + 64 * k] = static_cast<uint16_t>(f32_to_bf16_bits(o[k] * inv));
 }
 
 }  // namespace
@@ -625,24 +712,59 @@ int32_t prefill_check(const void* out, const void* q, const void* k_pool, const 
   return ok();
 }
 
+// Query tiles (workgroups without a key split) of a launch.
+int64_t prefill_tiles(int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int waves, int64_t* per_head) {
+  const int group = num_q_heads / num_kv_heads;
+  const int nw = (waves == 4 || waves == 8) && head_dim < 256 ? waves : default_waves(head_dim);
+  const int tm = nw / splits(head_dim) * rows_per_wave(head_dim);
+  *per_head = (static_cast<int64_t>(max_q_len) * group + tm - 1) / tm;
+  return *per_head * num_kv_heads;
+}
+
+// Key ranges per query tile: 1 when the query tiles alone give every CU a
+// workgroup (one resident per CU), else the smallest power of two, at most
+// kMaxKeySplit, that does. A function of the shapes and the CU count only.
+int prefill_key_splits(int64_t items, int cus) {
+  int s = 1;
+  while (s < kMaxKeySplit && items * s < cus) s <<= 1;
+  return s;
+}
+
+size_t prefill_ws_bytes(int ksplit, int32_t total_q, int32_t num_q_heads, int32_t head_dim) {
+  return ksplit > 1 ? static_cast<size_t>(ksplit) * total_q * num_q_heads * (head_dim + 2) * sizeof(float) : 0;
+}
+
 int32_t prefill_impl(void* out, const void* q, const void* k_pool, const void* v_pool,
                      const int32_t* block_tables, int32_t max_blocks_per_seq,
                      const int32_t* cu_q_lens, const int32_t* seq_lens, int32_t batch,
                      int32_t total_q, int32_t max_q_len, int32_t num_q_heads,
                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                      int32_t num_blocks, float scale, float k_scale, float v_scale,
-                     int32_t sliding_window, int esz, void* stream, int waves) {
+                     int32_t sliding_window, void* workspace, size_t workspace_bytes, int esz,
+                     void* stream, int waves) {
   if (int32_t rc = prefill_check(out, q, k_pool, v_pool, block_tables, max_blocks_per_seq,
                                  cu_q_lens, seq_lens, batch, total_q, max_q_len, num_q_heads,
                                  num_kv_heads, head_dim, block_size, num_blocks, scale, k_scale,
                                  v_scale, sliding_window))
     return rc;
+  if (workspace && !aligned16(workspace)) return fail(PAGED_ERR_INVALID_ARG, "misaligned workspace");
   if (batch == 0 || total_q == 0 || max_q_len == 0) return ok();
   const int group = num_q_heads / num_kv_heads;
   const int nw = (waves == 4 || waves == 8) && head_dim < 256 ? waves : default_waves(head_dim);
-  const int tm = nw / splits(head_dim) * rows_per_wave(head_dim);
-  const int64_t tiles = (static_cast<int64_t>(max_q_len) * group + tm - 1) / tm;
-  const int64_t items = tiles * num_kv_heads * batch;
+  int64_t tiles = 0;
+  const int64_t items1 = prefill_tiles(max_q_len, num_q_heads, num_kv_heads, head_dim, waves, &tiles) * batch;
+  int ksplit = 1;
+  if (workspace) {
+    const int cus = device_cu_count();
+    if (cus <= 0) return fail(PAGED_ERR_HIP, "cannot query the device compute-unit count");
+    ksplit = prefill_key_splits(items1, cus);
+    const size_t need = prefill_ws_bytes(ksplit, total_q, num_q_heads, head_dim);
+    if (workspace_bytes < need)
+      return fail(PAGED_ERR_INVALID_ARG, "workspace holds %zu bytes, the key split needs %zu", workspace_bytes,
+                  need);
+  }
+  const int64_t items = items1 * ksplit;
   if (items > (1LL << 30)) return fail(PAGED_ERR_INVALID_ARG, "problem too large");
   PrefillParams prm{};
   prm.out = static_cast<uint16_t*>(out);
@@ -660,10 +782,16 @@ int32_t prefill_impl(void* out, const void* q, const void* k_pool, const void* v
   prm.nb = num_blocks;
   prm.window = sliding_window;
   prm.tiles_per_head = static_cast<int32_t>(tiles);
+  prm.ksplit = ksplit;
   prm.work_items = static_cast<int32_t>(items);
   prm.per_xcd = static_cast<int32_t>((items + kNumXcd - 1) / kNumXcd);
+  prm.total_q = total_q;
   prm.scale_log2 = scale * 1.4426950408889634f * k_scale;
   prm.v_scale = v_scale;
+  if (ksplit > 1) {
+    prm.ws_acc = static_cast<float*>(workspace);
+    prm.ws_ml = prm.ws_acc + static_cast<size_t>(ksplit) * total_q * num_q_heads * head_dim;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid(static_cast<unsigned>(prm.per_xcd * kNumXcd));
   const dim3 block(nw * 64);
@@ -685,6 +813,18 @@ int32_t prefill_impl(void* out, const void* q, const void* k_pool, const void* v
     else nw == 8 ? launch(prefill_kernel<64, 2, 8>) : launch(prefill_kernel<64, 2, 4>);
   }
   tr.finish();
+  if (ksplit > 1) {
+    const dim3 rgrid(static_cast<unsigned>((static_cast<int64_t>(total_q) * num_q_heads + 3) / 4));
+    LaunchTrace rt(PAGED_KERNEL_PREFILL_REDUCE, s);
+    auto rlaunch = [&](auto kern) {
+      hipExtLaunchKernelGGL(kern, rgrid, dim3(256), 0, s, rt.start(), rt.stop(), 0, prm);
+    };
+    if (head_dim == 512) rlaunch(prefill_reduce_kernel<512>);
+    else if (head_dim == 256) rlaunch(prefill_reduce_kernel<256>);
+    else if (head_dim == 128) rlaunch(prefill_reduce_kernel<128>);
+    else rlaunch(prefill_reduce_kernel<64>);
+    rt.finish();
+  }
   return check_launch("paged_attn_prefill_chunk");
 }
 
@@ -698,12 +838,14 @@ extern "C" int32_t paged_attn_prefill_chunk(void* out, const void* q, const void
                                             int32_t num_q_heads, int32_t num_kv_heads,
                                             int32_t head_dim, int32_t block_size,
                                             int32_t num_blocks, float scale,
-                                            int32_t sliding_window, int32_t dtype, void* stream) {
+                                            int32_t sliding_window, void* workspace,
+                                            size_t workspace_bytes, int32_t dtype, void* stream) {
   if (dtype != PAGED_BF16)
     return fail(PAGED_ERR_DTYPE, "prefill takes bf16 (FP8 pools: paged_attn_prefill_chunk_fp8)");
   return prefill_impl(out, q, k_pool, v_pool, block_tables, max_blocks_per_seq, cu_q_lens,
                       seq_lens, batch, total_q, max_q_len, num_q_heads, num_kv_heads, head_dim,
-                      block_size, num_blocks, scale, 1.f, 1.f, sliding_window, 2, stream);
+                      block_size, num_blocks, scale, 1.f, 1.f, sliding_window, workspace,
+                      workspace_bytes, 2, stream);
 }
 
 extern "C" int32_t paged_attn_prefill_chunk_fp8(void* out, const void* q, const void* k_pool,
@@ -715,8 +857,30 @@ extern "C" int32_t paged_attn_prefill_chunk_fp8(void* out, const void* q, const 
                                                 int32_t head_dim, int32_t block_size,
                                                 int32_t num_blocks, float scale, float k_scale,
                                                 float v_scale, int32_t sliding_window,
+                                                void* workspace, size_t workspace_bytes,
                                                 void* stream) {
   return prefill_impl(out, q, k_pool, v_pool, block_tables, max_blocks_per_seq, cu_q_lens,
                       seq_lens, batch, total_q, max_q_len, num_q_heads, num_kv_heads, head_dim,
-                      block_size, num_blocks, scale, k_scale, v_scale, sliding_window, 1, stream);
+                      block_size, num_blocks, scale, k_scale, v_scale, sliding_window, workspace,
+                      workspace_bytes, 1, stream);
+}
+
+extern "C" int32_t paged_attn_prefill_chunk_workspace_bytes(int32_t batch, int32_t total_q,
+                                                            int32_t max_q_len, int32_t num_q_heads,
+                                                            int32_t num_kv_heads, int32_t head_dim,
+                                                            size_t* bytes) {
+  if (!bytes) return fail(PAGED_ERR_INVALID_ARG, "NULL argument");
+  *bytes = 0;
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256 && head_dim != 512)
+    return fail(PAGED_ERR_INVALID_ARG, "head_dim must be 64, 128, 256 or 512 (got %d)", head_dim);
+  if (num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads)
+    return fail(PAGED_ERR_INVALID_ARG, "need num_q_heads a positive multiple of num_kv_heads");
+  if (batch < 0 || total_q < 0 || max_q_len < 0) return fail(PAGED_ERR_INVALID_ARG, "bad size argument");
+  if (batch == 0 || total_q == 0 || max_q_len == 0) return ok();
+  const int cus = device_cu_count();
+  if (cus <= 0) return fail(PAGED_ERR_HIP, "cannot query the device compute-unit count");
+  int64_t tiles = 0;
+  const int64_t items = prefill_tiles(max_q_len, num_q_heads, num_kv_heads, head_dim, 0, &tiles) * batch;
+  *bytes = prefill_ws_bytes(prefill_key_splits(items, cus), total_q, num_q_heads, head_dim);
+  return ok();
 }

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define PAGEDKV_ABI_VERSION 1
+#define PAGEDKV_ABI_VERSION 2
 
 enum {
   PAGED_OK = 0,
@@ -256,15 +256,37 @@ int32_t paged_attn_decode_noalloc(void* out, const void* q, const void* k_pool, 
  *   out, q       : device bf16, [total_q][num_q_heads][head_dim]
  *   cu_q_lens    : device int32 [batch + 1], cu_q_lens[0] = 0, nondecreasing,
  *                  cu_q_lens[batch] = total_q, each chunk <= max_q_len
- *   seq_lens     : device int32 [batch], seq_lens[b] >= chunk length of b */
+ *   seq_lens     : device int32 [batch], seq_lens[b] >= chunk length of b
+ *   workspace    : NULL, or device memory (16-byte aligned, caller-owned, not
+ *                  read before it is written) of at least
+ *                  paged_attn_prefill_chunk_workspace_bytes(...) bytes for the
+ *                  same shapes. With NULL one workgroup covers each tile of
+ *                  query rows over its whole key range. With a workspace, when
+ *                  the query tiles are fewer than the device's compute units
+ *                  (few rows or few heads, e.g. one GPU's share of KV heads),
+ *                  the key range of every tile is cut into S near-equal parts
+ *                  (S the smallest power of two up to 16 that gives every CU a
+ *                  workgroup), each part's unnormalised output and (max, sum)
+ *                  go to the workspace and a second kernel combines the S
+ *                  parts of each (query, head) like the decode reduce. The
+ *                  result is the same attention up to float rounding.
+ *                  PAGED_ERR_INVALID_ARG when it is misaligned or too small. */
 int32_t paged_attn_prefill_chunk(void* out, const void* q, const void* k_pool,
                                  const void* v_pool, const int32_t* block_tables,
                                  int32_t max_blocks_per_seq, const int32_t* cu_q_lens,
                                  const int32_t* seq_lens, int32_t batch, int32_t total_q,
                                  int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                                 float scale, int32_t sliding_window, int32_t dtype,
-                                 void* stream);
+                                 float scale, int32_t sliding_window, void* workspace,
+                                 size_t workspace_bytes, int32_t dtype, void* stream);
+
+/* Bytes of workspace paged_attn_prefill_chunk (and _fp8) use for these shapes
+ * on the current device (0: no key split, the workspace may be NULL). Needs a
+ * device (the split depends on its compute-unit count): PAGED_ERR_HIP without one. */
+int32_t paged_attn_prefill_chunk_workspace_bytes(int32_t batch, int32_t total_q,
+                                                 int32_t max_q_len, int32_t num_q_heads,
+                                                 int32_t num_kv_heads, int32_t head_dim,
+                                                 size_t* bytes);
 
 /* paged_attn_prefill_chunk over FP8 pools (K, V as in paged_attn_decode_fp8);
  * q and out bf16. Same arguments and errors otherwise. */
@@ -275,16 +297,18 @@ int32_t paged_attn_prefill_chunk_fp8(void* out, const void* q, const void* k_poo
                                      int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
                                      int32_t head_dim, int32_t block_size, int32_t num_blocks,
                                      float scale, float k_scale, float v_scale,
-                                     int32_t sliding_window, void* stream);
+                                     int32_t sliding_window, void* workspace,
+                                     size_t workspace_bytes, void* stream);
 
 /* One continuous-batching step over one layer (batching-perf-path doc,
  * current state: chunked prefill of joining requests interleaved with the
  * running decode rows). Rows [0, num_decode_rows) are decode rows with one
  * query each (cu_q_lens[b] == b for b <= num_decode_rows: query b is row b's
  * newest position); rows [num_decode_rows, batch) are prefill chunks. The
- * result is exactly that of paged_attn_prefill_chunk over all rows (a decode
- * row is a chunk of one); the decode rows run through the split-K decode
- * kernels on `stream`, the chunk rows through the prefill kernel on a second
+ * result is the attention paged_attn_prefill_chunk computes over all rows (a
+ * decode row is a chunk of one), up to float rounding; the decode rows run
+ * through the split-K decode kernels on `stream`, the chunk rows through the
+ * prefill kernel (no key split: the decode fills the other CUs) on a second
  * stream the library keeps per device, so both run at once; `stream` waits
  * for both before anything enqueued after the call. The first call on a
  * device creates that stream and two events (keep it outside graph capture);
@@ -320,7 +344,8 @@ enum {
   PAGED_KERNEL_DECODE_PARTIAL = 2,
   PAGED_KERNEL_DECODE_REDUCE = 3,
   PAGED_KERNEL_PREFILL = 4,
-  PAGED_KERNEL_COUNT = 5
+  PAGED_KERNEL_PREFILL_REDUCE = 5,
+  PAGED_KERNEL_COUNT = 6
 };
 
 /* on != 0: from now on, every launch records a start and an end event on its

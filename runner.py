@@ -115,9 +115,23 @@ def gpu_workspace(wl, dev, partition_tokens=None, max_seq_len=None):
     return torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
 
 
+def prefill_workspace(wl):
+    """Workspace of the prefill's key split for a chunk-only workload (None when
+    the library would not split these shapes on this device)."""
+    import torch
+
+    import block_paged_kv_amd as pk
+
+    need = pk.paged_attn_prefill_chunk_workspace_bytes(wl.batch, int(wl.chunk_lens.sum()),
+                                                       int(wl.chunk_lens.max()), wl.hq, wl.hkv, wl.head_dim)
+    return torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
+
+
 def gpu_step(wl, dev, outs=None, workspace=None, partition_tokens=None, max_seq_len=None,
-             layers=None):
-    """One pass of the hot path: the step's KV writes, then attention per layer."""
+             layers=None, prefill_split=False):
+    """One pass of the hot path: the step's KV writes, then attention per layer.
+    ``prefill_split``: chunk-only workloads pass the prefill a workspace (key
+    split where the library's rule asks for one)."""
     import torch
 
     import block_paged_kv_amd as pk
@@ -137,6 +151,7 @@ def gpu_step(wl, dev, outs=None, workspace=None, partition_tokens=None, max_seq_
             pk.paged_kv_write(d["k_pool"], d["v_pool"], d["step_k"], d["step_v"], d["step_slots"])
     part = wl.partition_tokens if partition_tokens is None else partition_tokens
     msl = decode_max_seq_len(wl) if max_seq_len is None else max_seq_len
+    pws = prefill_workspace(wl) if prefill_split and wl.kind == "prefill" and not wl.num_decode else None
     for n in names:
         d = dev[n]
         if wl.kind == "prefill" and wl.num_decode:
@@ -158,11 +173,11 @@ def gpu_step(wl, dev, outs=None, workspace=None, partition_tokens=None, max_seq_
             pk.paged_attn_prefill_chunk_fp8(outs[n], d["q"], d["k_pool"], d["v_pool"], d["tables"],
                                             dev["_cu_q"], dev["_seq_lens"], int(wl.chunk_lens.max()),
                                             wl.scale, d["k_scale"], d["v_scale"],
-                                            sliding_window=d["window"])
+                                            sliding_window=d["window"], workspace=pws)
         else:
             pk.paged_attn_prefill_chunk(outs[n], d["q"], d["k_pool"], d["v_pool"], d["tables"],
                                         dev["_cu_q"], dev["_seq_lens"], int(wl.chunk_lens.max()),
-                                        wl.scale, sliding_window=d["window"])
+                                        wl.scale, sliding_window=d["window"], workspace=pws)
     return outs
 
 

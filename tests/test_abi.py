@@ -71,18 +71,18 @@ def test_decode_argument_errors():
 def test_prefill_argument_errors():
     L = pk.lib
     rc = L.paged_attn_prefill_chunk(None, None, None, None, None, 4, None, None, 1, 8, 8, 8, 8, 128,
-                                    16, 8, 0.1, 0, pk.PAGED_F32, None)
+                                    16, 8, 0.1, 0, None, 0, pk.PAGED_F32, None)
     assert rc == pk.PAGED_ERR_DTYPE
     rc = L.paged_attn_prefill_chunk(None, None, None, None, None, 4, None, None, 1, 8, 8, 8, 3, 128,
-                                    16, 8, 0.1, 0, pk.PAGED_BF16, None)
+                                    16, 8, 0.1, 0, None, 0, pk.PAGED_BF16, None)
     assert rc == pk.PAGED_ERR_INVALID_ARG
     rc = L.paged_attn_prefill_chunk(None, None, None, None, None, 4, None, None, 1, 0, 8, 8, 8, 128,
-                                    16, 8, 0.1, 0, pk.PAGED_BF16, None)
+                                    16, 8, 0.1, 0, None, 0, pk.PAGED_BF16, None)
     assert rc == pk.PAGED_OK
     # negative or non-finite scale
     for bad in (-0.1, float("nan")):
         rc = L.paged_attn_prefill_chunk(None, None, None, None, None, 4, None, None, 1, 8, 8, 8, 8, 128,
-                                        16, 8, bad, 0, pk.PAGED_BF16, None)
+                                        16, 8, bad, 0, None, 0, pk.PAGED_BF16, None)
         assert rc == pk.PAGED_ERR_INVALID_ARG
 
 
@@ -116,7 +116,7 @@ def test_head_dim_512_limits():
     assert e.value.code == pk.PAGED_ERR_INVALID_ARG
     for d in (96, 384, 1024):
         rc = pk.lib.paged_attn_prefill_chunk(None, None, None, None, None, 4, None, None, 1, 8, 8, 8, 8, d,
-                                             16, 8, 0.1, 0, pk.PAGED_BF16, None)
+                                             16, 8, 0.1, 0, None, 0, pk.PAGED_BF16, None)
         assert rc == pk.PAGED_ERR_INVALID_ARG
         assert b"head_dim" in pk.lib.paged_last_error()
     assert pk.lib.paged_kv_write(None, None, None, None, None, 1, 8, 16, 1, 1024, 1, None) == \
@@ -168,8 +168,31 @@ def test_scale_must_be_positive():
                                  pk.PAGED_BF16, None)
         assert rc == pk.PAGED_ERR_INVALID_ARG and b"scale" in L.paged_last_error()
         rc = L.paged_attn_prefill_chunk(16, 16, 16, 16, 16, 4, 16, 16, 1, 8, 8, 4, 2, 128, 16, 8, scale, 0,
-                                        pk.PAGED_BF16, None)
+                                        None, 0, pk.PAGED_BF16, None)
         assert rc == pk.PAGED_ERR_INVALID_ARG and b"scale" in L.paged_last_error()
+
+
+def test_prefill_workspace_checks():
+    L = pk.lib
+    # argument errors come before the device query; the rule itself needs a device
+    with pytest.raises(pk.PagedError) as e:
+        pk.paged_attn_prefill_chunk_workspace_bytes(1, 8, 8, 8, 8, 96)
+    assert e.value.code == pk.PAGED_ERR_INVALID_ARG
+    with pytest.raises(pk.PagedError) as e:
+        pk.paged_attn_prefill_chunk_workspace_bytes(1, 8, 8, 6, 4, 128)
+    assert e.value.code == pk.PAGED_ERR_INVALID_ARG
+    assert pk.paged_attn_prefill_chunk_workspace_bytes(0, 0, 0, 8, 8, 128) == 0
+    with pytest.raises(pk.PagedError) as e:
+        pk.paged_attn_prefill_chunk_workspace_bytes(1, 2048, 2048, 4, 1, 128)
+    assert e.value.code == pk.PAGED_ERR_HIP
+    assert L.paged_attn_prefill_chunk_workspace_bytes(1, 8, 8, 8, 8, 128, None) == pk.PAGED_ERR_INVALID_ARG
+    # a misaligned workspace is refused before anything is enqueued
+    rc = L.paged_attn_prefill_chunk(16, 16, 16, 16, 16, 4, 16, 16, 1, 8, 8, 4, 2, 128, 16, 8, 0.1, 0,
+                                    8, 1 << 20, pk.PAGED_BF16, None)
+    assert rc == pk.PAGED_ERR_INVALID_ARG and b"workspace" in L.paged_last_error()
+    rc = L.paged_attn_prefill_chunk_fp8(16, 16, 16, 16, 16, 4, 16, 16, 1, 8, 8, 4, 2, 128, 16, 8, 0.1, 1.0,
+                                        1.0, 0, 24, 1 << 20, None)
+    assert rc == pk.PAGED_ERR_INVALID_ARG and b"workspace" in L.paged_last_error()
 
 
 def test_library_rule_needs_a_device_here():

@@ -145,6 +145,11 @@ def test_fp8_decode_small(pk, name, kw, step):
     run_case(pk, synth.make(name, kv_dtype="fp8", **kw), label="fp8-decode", **step)
 
 
+def test_fp8_decode_one_row_many_partitions(pk):
+    # one row of the hybrid workload: 256 partitions, the wide reduce
+    run_case(pk, synth.make("hybrid", batch=1, kv_dtype="fp8"), label="fp8-decode-many-parts")
+
+
 @pytest.mark.parametrize("name", ["qwen3", "mixed", "hybrid"])
 def test_fp8_decode_full_size(pk, name):
     run_case(pk, synth.make(name, kv_dtype="fp8"), label="fp8-decode-full")
@@ -161,6 +166,16 @@ def test_fp8_decode_full_size(pk, name):
 ], ids=[str(i) for i in range(7)])
 def test_fp8_prefill_small(pk, kw):
     run_case(pk, synth.make("prefill", kv_dtype="fp8", **kw), label="fp8-prefill")
+
+
+@pytest.mark.parametrize("kw", [
+    dict(batch=3, context=[70, 33, 0], chunk=[40, 9, 17], num_blocks=64),
+    dict(batch=2, context=[300, 64], chunk=[150, 100], num_blocks=64, hq=8, hkv=1, head_dim=512, window=37),
+], ids=["d128", "d512"])
+def test_fp8_prefill_key_split(pk, kw):
+    wl = synth.make("prefill", kv_dtype="fp8", **kw)
+    assert runner.prefill_workspace(wl) is not None
+    run_case(pk, wl, label="fp8-prefill-split", prefill_split=True)
 
 
 @pytest.mark.timeout(600)  # the whole output against the float64 oracle on the host

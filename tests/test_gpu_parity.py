@@ -278,6 +278,25 @@ def test_decode_long_row(pk):
              label="decode-128k")
 
 
+# More partitions per row than one chunk of the reduce holds (64; 32 at
+# head_dim 512): the wide reduce, four waves taking chunks in parallel (more
+# than four chunks: a wave takes several in turn).
+MANY_PARTS = [
+    ("hybrid", dict(batch=1), {}),                        # one GPU's share of 8: 256 partitions
+    ("hybrid", dict(batch=1, head_dim=512), {}),          # head_dim 512: 256 partitions
+    ("tiny", dict(context=[1500, 2000], prefix=32), dict(partition_tokens=16)),  # float32: 125
+    ("mixed", dict(batch=3, context=(3000, 5000), prefix=100, hq=4, hkv=2, num_blocks=1200),
+     dict(partition_tokens=16)),                          # up to 313 partitions: five chunks
+    ("hybrid", dict(batch=2, context=700, window=64, head_dim=512, sliding_blocks=40, num_blocks=200),
+     dict(partition_tokens=16)),                          # 44 partitions at head_dim 512
+]
+
+
+@pytest.mark.parametrize("name,kw,step", MANY_PARTS, ids=[f"{n}-{i}" for i, (n, _, _) in enumerate(MANY_PARTS)])
+def test_decode_many_partitions(pk, name, kw, step):
+    run_case(pk, synth.make(name, **kw), label="decode-many-parts", **step)
+
+
 def test_decode_partition_limit(pk):
     # 65535 partitions of 16 tokens (the grid's z limit): all but the first few
     # of every row are empty
@@ -457,6 +476,50 @@ K_GROWTH = [
 @pytest.mark.parametrize("name,kw", K_GROWTH, ids=[f"{n}-{i}" for i, (n, _) in enumerate(K_GROWTH)])
 def test_growing_scores_rescale(pk, name, kw):
     run_case(pk, synth.make(name, k_growth=32, **kw), label="k-growth")
+
+
+# Key split: with a workspace and fewer query tiles than CUs, every tile's key
+# range is cut into parts whose partials the prefill reduce combines. All of
+# these shapes split (empty parts included: a tile with fewer key tiles than
+# parts), sliding windows, GQA 1..16, block sizes 8..64, head dims 64..512.
+KEY_SPLIT = [("prefill", kw) for kw in PREFILL_SMALL] + [
+    ("hprefill", HPREFILL_SMALL[0]), ("hprefill", HPREFILL_SMALL[2]), PREFILL_D512[0], PREFILL_D512[1],
+    PREFILL_D512[5], ("prefill", dict(K_GROWTH[0][1], k_growth=32)),
+    ("prefill", dict(K_GROWTH[2][1], k_growth=32)),
+]
+
+
+@pytest.mark.parametrize("name,kw", KEY_SPLIT, ids=[f"{n}-{i}" for i, (n, _) in enumerate(KEY_SPLIT)])
+def test_prefill_key_split(pk, name, kw):
+    wl = synth.make(name, **kw)
+    assert runner.prefill_workspace(wl) is not None, "expected a key split for this shape"
+    run_case(pk, wl, label="prefill-split", prefill_split=True)
+
+
+@pytest.mark.timeout(600)  # the whole output against the float64 oracle on the host
+def test_prefill_key_split_shard_shape_every_row(pk):
+    # One GPU's share of the chunked prefill over 8 GPUs by KV head: 4 query
+    # heads on 1 KV head, 32 query tiles, each key range cut in 8.
+    wl = synth.make("prefill", hq=4, hkv=1)
+    assert runner.prefill_workspace(wl) is not None
+    run_case(pk, wl, label="prefill-shard8-split", prefill_split=True)
+
+
+def test_prefill_workspace_bytes_rule(pk):
+    import torch
+
+    announce("prefill workspace bytes")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    rows_per_wg = {64: 256, 128: 256, 256: 128, 512: 64}
+    for B, T, C, hq, hkv, d in [(1, 2048, 2048, 32, 8, 128), (1, 2048, 2048, 4, 1, 128),
+                                (4, 8192, 2048, 8, 1, 256), (2, 100, 64, 8, 1, 512), (1, 1, 1, 4, 2, 64),
+                                (3, 300, 100, 16, 2, 64)]:
+        items = -(-C * (hq // hkv) // rows_per_wg[d]) * hkv * B
+        S = 1
+        while S < 16 and items * S < cus:
+            S *= 2
+        expect = 0 if S == 1 else S * T * hq * (d + 2) * 4
+        assert pk.paged_attn_prefill_chunk_workspace_bytes(B, T, C, hq, hkv, d) == expect, (B, T, C, hq, hkv, d)
 
 
 # One continuous-batching step: decode rows (split-K decode kernels on the
