@@ -846,8 +846,9 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_lds_kernel(D
 
 // Combine each (row, query head) pair's partitions. WPP waves serve one pair
 // (a 256-thread workgroup serves 4 / WPP pairs); lane l of the pair's wave w
-// owns head_dim columns 64 w + l + 64 WPP k, k < CPT = D / (64 WPP).
-// Partitions are taken in chunks of CH = 64 / CPT (at most 64): lane i of
+// owns the CPT = D / (64 WPP) consecutive head_dim columns starting at
+// CPT (64 w + l), read and written as one or two wide accesses.
+// Partitions are taken in chunks of CH = reduce_chunk(CPT): lane i of
 // every wave holds the chunk's partition i (max, sum). The launcher picks the
 // fewest waves per pair for which a row's partitions fit one chunk, so that
 // the row length, the (max, sum) pairs and every accumulator are requested
@@ -856,11 +857,57 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_lds_kernel(D
 // before the store. Longer rows take further chunks, combined in order with
 // an online maximum; the result does not depend on how many empty partitions
 // follow the live ones.
+// Partitions per chunk of decode_reduce_kernel with CPT columns per lane: 64
+// accumulator registers, 128 from four columns per lane on (one wave then
+// covers a pair at head_dim 256 with 16-byte loads; more registers at one or
+// two columns per lane measured slower).
+constexpr int reduce_chunk(int cpt) { return cpt >= 4 ? 128 / cpt : 64 / cpt; }
+
+// CPT consecutive floats from p (16-, 8- or 4-byte aligned), or zeros.
+template <int CPT>
+__device__ __forceinline__ void load_cols(float* dst, bool ok, const float* p) {
+  if constexpr (CPT % 4 == 0) {
+#pragma unroll
+    for (int k = 0; k < CPT; k += 4) {
+      const floatx4_t v = ok ? *reinterpret_cast<const floatx4_t*>(p + k) : floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[k + e] = v[e];
+    }
+  } else if constexpr (CPT == 2) {
+    const float2 v = ok ? *reinterpret_cast<const float2*>(p) : make_float2(0.f, 0.f);
+    dst[0] = v.x;
+    dst[1] = v.y;
+  } else {
+    dst[0] = ok ? *p : 0.f;
+  }
+}
+
+// CPT consecutive outputs at element index i of out (bf16 for ESZ <= 2, else
+// float32), written as one or two wide stores.
+template <int ESZ, int CPT>
+__device__ __forceinline__ void store_cols(void* out, size_t i, const float* v) {
+  if constexpr (ESZ <= 2 && CPT >= 2) {
+    uint32_t w[CPT / 2];
+#pragma unroll
+    for (int k = 0; k < CPT / 2; ++k) w[k] = pack_bf16x2(v[2 * k], v[2 * k + 1]);
+    uint16_t* o = static_cast<uint16_t*>(out) + i;
+    if constexpr (CPT == 2) {
+      *reinterpret_cast<uint32_t*>(o) = w[0];
+    } else {
+#pragma unroll
+      for (int k = 0; k < CPT / 2; k += 2) *reinterpret_cast<uint2*>(o + 2 * k) = make_uint2(w[k], w[k + 1]);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) store_out<ESZ>(out, i + k, v[k]);
+  }
+}
+
 template <int ESZ, int D, int CPT>
 __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeParams a) {
   constexpr float kNegInf = -INFINITY;
   constexpr int WPP = D / (64 * CPT);          // waves per pair
-  constexpr int CH = 64 / CPT;                 // partitions per chunk
+  constexpr int CH = reduce_chunk(CPT);        // partitions per chunk
   static_assert(WPP >= 1 && WPP <= 4 && D == 64 * CPT * WPP, "bad reduce shape");
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -868,7 +915,7 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeParams a) {
   const int h = blockIdx.x * (4 / WPP) + wave / WPP;
   if (h >= a.hq) return;
   const int pair = b * a.hq + h;
-  const int c0l = (wave % WPP) * 64 + lane;    // first column of this lane
+  const int c0l = ((wave % WPP) * 64 + lane) * CPT;  // this lane's CPT consecutive columns
   const int P = a.max_parts;
   const float* ml = a.ws_ml + static_cast<size_t>(pair) * P * 2;
   const float* acc = a.ws_acc + static_cast<size_t>(pair) * P * D;
@@ -878,10 +925,7 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeParams a) {
   float2 mlc = lane < CH && lane < P ? *reinterpret_cast<const float2*>(ml + 2 * lane) : make_float2(kNegInf, 0.f);
   float x[CH][CPT];
 #pragma unroll
-  for (int u = 0; u < CH; ++u)
-#pragma unroll
-    for (int k = 0; k < CPT; ++k)
-      x[u][k] = u < P ? acc[static_cast<size_t>(u) * D + c0l + 64 * WPP * k] : 0.f;
+  for (int u = 0; u < CH; ++u) load_cols<CPT>(x[u], u < P, acc + static_cast<size_t>(u) * D + c0l);
 
   const int lo = a.window > 0 ? max(0, n - a.window) : 0;
   const int s0 = (lo >> a.bs_log2) << a.bs_log2;
@@ -898,10 +942,7 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeParams a) {
       mlc = lane < CH && pl < P ? *reinterpret_cast<const float2*>(ml + 2 * static_cast<size_t>(pl))
                                 : make_float2(kNegInf, 0.f);
 #pragma unroll
-      for (int u = 0; u < CH; ++u)
-#pragma unroll
-        for (int k = 0; k < CPT; ++k)
-          x[u][k] = c0 + u < P ? acc[static_cast<size_t>(c0 + u) * D + c0l + 64 * WPP * k] : 0.f;
+      for (int u = 0; u < CH; ++u) load_cols<CPT>(x[u], c0 + u < P, acc + static_cast<size_t>(c0 + u) * D + c0l);
     }
     const bool live = lane < CH && c0 + lane < np;
     const float mp = live ? mlc.x : kNegInf;
@@ -931,17 +972,17 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeParams a) {
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
-  for (int k = 0; k < CPT; ++k)
-    store_out<ESZ>(a.out, static_cast<size_t>(pair) * D + c0l + 64 * WPP * k, o[k] * inv);
+  for (int k = 0; k < CPT; ++k) o[k] *= inv;
+  store_cols<ESZ, CPT>(a.out, static_cast<size_t>(pair) * D + c0l, o);
 }
 
-// Rows with more partitions than one chunk of the kernel above holds (64,
-// or 32 at head_dim 512): a workgroup per (row, query head, 64 columns), lane
+// Rows with more partitions than one chunk of the kernel above holds (64): a
+// workgroup per (row, query head, 64 columns), lane
 // l owning one column; its four waves take chunks of 64 partitions w, w + 4,
 // ... (every wave's first chunk requested before the row length is known),
 // each combines its chunks with an online maximum, and the four results are
-// combined through LDS. Up to 256 partitions (C4's 32768-token rows at one row
-// per GPU) this is one round trip to memory instead of one per chunk.
+// combined through LDS. Up to 256 partitions (a 32768-token row alone on
+// the device) this is one round trip to memory instead of one per chunk.
 template <int ESZ, int D>
 __global__ __launch_bounds__(256) void decode_reduce_wide_kernel(DecodeParams a) {
   constexpr float kNegInf = -INFINITY;
@@ -1163,7 +1204,7 @@ void launch_partial_any(const DecodeParams& prm, int kv_esz, int d, int gt, dim3
 int reduce_waves_per_pair(int d, int max_parts) {
   for (int wpp = 1; wpp <= 4; wpp *= 2) {
     const int cpt = d / (64 * wpp);
-    if (cpt >= 1 && cpt * max_parts <= 64) return wpp;
+    if (cpt >= 1 && max_parts <= reduce_chunk(cpt)) return wpp;
   }
   return 0;
 }
