@@ -344,7 +344,9 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
   // The K fragment reads run PF fragments ahead of the products and the key
   // sub-tiles' accumulation chains alternate; scheduling barriers keep that
   // order (left to itself the compiler waits on each read right before its
-  // product, which a second wave on the SIMD can only partly hide). With the
+  // product, which a second wave on the SIMD can only partly hide). Eight
+  // ahead from head_dim 256, where the waves wait on LDS results and the
+  // registers allow it, four below. With the
   // head dimension split, the wave's k-steps start at half * KSW: whole
   // groups of four, so the half only moves the row base.
   auto tile_s = [&](Scores& sc, const uint16_t* ks_buf) {
@@ -353,7 +355,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
       const int pos = (((4 * (ks & 3) + lg) ^ swz_k(lq)) << 3) + (ks >> 2) * 128;
       return *reinterpret_cast<const uint4*>(krow + t4 * 16 * D + pos);
     };
-    constexpr int PF = 4;
+    constexpr int PF = D >= 256 ? 8 : 4;
     constexpr int NR = NS * KSW;  // K fragments of one tile; fragment u: sub-tile u % NS, step u / NS
     uint4 kf[PF + 1];
 #pragma unroll
@@ -484,7 +486,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
         const uint2 v1 = ds_read_tr16(vbase + 16 * D + vc);
         return make_uint4(v0.x, v0.y, v1.x, v1.y);
       };
-      constexpr int PF = 4;
+      constexpr int PF = D >= 256 ? 8 : 4;
       constexpr int NV = NK * NTW;
       uint4 vf[PF + 1];
 #pragma unroll
