@@ -75,7 +75,7 @@ extern "C" int32_t paged_attn_mixed(void* out, const void* q, const void* k_pool
                             max_blocks_per_seq, cu_q_lens + nd, seq_lens + nd, np, total_q - nd,
                             max_q_len, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                             scale, k_scale, v_scale, sliding_window, /*workspace=*/nullptr, 0, esz,
-                            side.get(), /*waves=*/4);
+                            side.get(), /*waves=*/4, /*beside_decode=*/true);
   if (rc == PAGED_OK)
     rc = decode_impl(out, q, k_pool, v_pool, block_tables, max_blocks_per_seq, seq_lens, nd,
                      num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, k_scale,
