@@ -538,59 +538,59 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
   // An empty key range (key split only) leaves the row state as it starts:
   // no keys, weight zero in the reduce.
   if (kt_begin <= kt_end) {
-  int ent_next = load_entries(kt_begin + 1);
-  uint64_t absent_next = stage_load(kt_begin, load_entries(kt_begin), 0);
-  stage_store(0);
-  __syncthreads();
-
-  // Each tile through all three parts, tile kt+1 streaming into the other
-  // buffer meanwhile. The S^T burst runs at raised wave priority, so that a
-  // wave issuing back-to-back MFMAs is not held up by the softmax work of the
-  // other wave on its SIMD, which fills the gaps.
-  Scores sc;
-  for (int kt = kt_begin; kt <= kt_end; ++kt) {
-    const int buf = (kt - kt_begin) & 1;
-    const bool has_next = kt < kt_end;
-    const uint64_t absent = absent_next;
-    if (has_next) {
-      absent_next = stage_load(kt + 1, ent_next, buf ^ 1);
-      ent_next = load_entries(kt + 2);
-    }
-    const int ts = kt * kTileN;
-    __builtin_amdgcn_s_setprio(1);
-    tile_s(sc, k_s[buf]);
-    __builtin_amdgcn_s_setprio(0);
-    if constexpr (SPL > 1) {
-      // The partner wave (same rows, other half of head_dim) holds the rest
-      // of each score: exchange through LDS and add. Both waves add the same
-      // two values, so both hold bit-identical scores (and probabilities).
-#pragma unroll
-      for (int j = 0; j < JT; ++j)
-#pragma unroll
-        for (int t4 = 0; t4 < NS; ++t4) exch[wave][j * NS + t4][lane] = sc[j][t4];
-      __syncthreads();
-      const int partner = wave ^ RG;
-#pragma unroll
-      for (int j = 0; j < JT; ++j)
-#pragma unroll
-        for (int t4 = 0; t4 < NS; ++t4) {
-          const floatx4_t other = exch[partner][j * NS + t4][lane];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sc[j][t4][i] += other[i];
-        }
-    }
-    tile_softmax(sc, needs_mask(ts) || absent != 0, ts, absent);
-    // FP8 codes up to head_dim 128 are widened into the other buffer before
-    // the P.V part, so the LDS stores drain under it rather than before the
-    // barrier (their loads have landed by then; measured 5% faster, and no
-    // faster at head_dim 256 and 512). Direct copies (bf16) only need their
-    // wait, as late as possible.
-    constexpr bool kEarlyStore = ESZ == 1 && D <= 128;
-    if (kEarlyStore && has_next) stage_store(buf ^ 1);
-    tile_pv(v_s[buf]);
-    if (!kEarlyStore && has_next) stage_store(buf ^ 1);
+    int ent_next = load_entries(kt_begin + 1);
+    uint64_t absent_next = stage_load(kt_begin, load_entries(kt_begin), 0);
+    stage_store(0);
     __syncthreads();
-  }
+
+    // Each tile through all three parts, tile kt+1 streaming into the other
+    // buffer meanwhile. The S^T burst runs at raised wave priority, so that a
+    // wave issuing back-to-back MFMAs is not held up by the softmax work of the
+    // other wave on its SIMD, which fills the gaps.
+    Scores sc;
+    for (int kt = kt_begin; kt <= kt_end; ++kt) {
+      const int buf = (kt - kt_begin) & 1;
+      const bool has_next = kt < kt_end;
+      const uint64_t absent = absent_next;
+      if (has_next) {
+        absent_next = stage_load(kt + 1, ent_next, buf ^ 1);
+        ent_next = load_entries(kt + 2);
+      }
+      const int ts = kt * kTileN;
+      __builtin_amdgcn_s_setprio(1);
+      tile_s(sc, k_s[buf]);
+      __builtin_amdgcn_s_setprio(0);
+      if constexpr (SPL > 1) {
+        // The partner wave (same rows, other half of head_dim) holds the rest
+        // of each score: exchange through LDS and add. Both waves add the same
+        // two values, so both hold bit-identical scores (and probabilities).
+#pragma unroll
+        for (int j = 0; j < JT; ++j)
+#pragma unroll
+          for (int t4 = 0; t4 < NS; ++t4) exch[wave][j * NS + t4][lane] = sc[j][t4];
+        __syncthreads();
+        const int partner = wave ^ RG;
+#pragma unroll
+        for (int j = 0; j < JT; ++j)
+#pragma unroll
+          for (int t4 = 0; t4 < NS; ++t4) {
+            const floatx4_t other = exch[partner][j * NS + t4][lane];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sc[j][t4][i] += other[i];
+          }
+      }
+      tile_softmax(sc, needs_mask(ts) || absent != 0, ts, absent);
+      // FP8 codes up to head_dim 128 are widened into the other buffer before
+      // the P.V part, so the LDS stores drain under it rather than before the
+      // barrier (their loads have landed by then; measured 5% faster, and no
+      // faster at head_dim 256 and 512). Direct copies (bf16) only need their
+      // wait, as late as possible.
+      constexpr bool kEarlyStore = ESZ == 1 && D <= 128;
+      if (kEarlyStore && has_next) stage_store(buf ^ 1);
+      tile_pv(v_s[buf]);
+      if (!kEarlyStore && has_next) stage_store(buf ^ 1);
+      __syncthreads();
+    }
   }
 
   if (a.ksplit > 1) {
