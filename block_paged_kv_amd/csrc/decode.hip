@@ -844,19 +844,6 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_lds_kernel(D
 }
 
 
-// Combine each (row, query head) pair's partitions. WPP waves serve one pair
-// (a 256-thread workgroup serves 4 / WPP pairs); lane l of the pair's wave w
-// owns the CPT = D / (64 WPP) consecutive head_dim columns starting at
-// CPT (64 w + l), read and written as one or two wide accesses.
-// Partitions are taken in chunks of CH = reduce_chunk(CPT): lane i of
-// every wave holds the chunk's partition i (max, sum). The launcher picks the
-// fewest waves per pair for which a row's partitions fit one chunk, so that
-// the row length, the (max, sum) pairs and every accumulator are requested
-// together, before the row's live partition count is known (entries past it
-// are fetched but never used, only selected away): one round trip to memory
-// before the store. Longer rows take further chunks, combined in order with
-// an online maximum; the result does not depend on how many empty partitions
-// follow the live ones.
 // Partitions per chunk of decode_reduce_kernel with CPT columns per lane: 64
 // accumulator registers, 128 from four columns per lane on (one wave then
 // covers a pair at head_dim 256 with 16-byte loads; more registers at one or
@@ -903,6 +890,20 @@ __device__ __forceinline__ void store_cols(void* out, size_t i, const float* v) 
   }
 }
 
+// Combine each (row, query head) pair's partitions. WPP waves serve one pair
+// (a 256-thread workgroup serves 4 / WPP pairs); lane l of the pair's wave w
+// owns the CPT = D / (64 WPP) consecutive head_dim columns starting at
+// CPT (64 w + l), read and written as one or two wide accesses.
+// Partitions are taken in chunks of CH = reduce_chunk(CPT): lane i of
+// every wave holds the chunk's partition i (max, sum). The launcher picks the
+// fewest waves per pair for which a row's partitions fit one chunk, so that
+// the row length, the (max, sum) pairs and every accumulator are requested
+// together, before the row's live partition count is known (entries past it
+// are fetched but never used, only selected away): one round trip to memory
+// before the store. (The kernel also takes further chunks in order, combined
+// with an online maximum, but the launcher sends rows with more partitions
+// than a chunk to the wide kernel below.) The result does not depend on how
+// many empty partitions follow the live ones.
 template <int ESZ, int D, int CPT>
 __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeParams a) {
   constexpr float kNegInf = -INFINITY;
@@ -1197,8 +1198,6 @@ void launch_partial_any(const DecodeParams& prm, int kv_esz, int d, int gt, dim3
   }
 }
 
-// Waves per (row, query head) for the reduce: the fewest for which the
-// pair's partitions (up to 64) fit one chunk of 64 / columns-per-lane.
 // Waves per (row, query head) of decode_reduce_kernel: the fewest for which a
 // row's partitions fit one chunk; 0 when none does (decode_reduce_wide_kernel).
 int reduce_waves_per_pair(int d, int max_parts) {
