@@ -582,6 +582,8 @@ def test_prefill_chunk_of_one_matches_decode(pk):
     ("prefill", dict(batch=2, context=[300, 64], chunk=[150, 100], num_blocks=64, hq=8, hkv=1, head_dim=512)),
     ("mixedstep", dict(batch=3, context=(200, 600), chunk=[90], prefix=[150], num_blocks=200, hq=8, hkv=1,
                        head_dim=512, part=128)),
+    # the prefill with its key split (a workspace; two kernels per call)
+    ("prefill", dict(batch=2, context=[300, 64], chunk=[150, 100], num_blocks=64, hq=8, hkv=2, split=True)),
 ])
 def test_step_graph_replays_match_eager(pk, name, kw):
     """The step (KV write + attention) captured in a HIP graph, with the
@@ -589,7 +591,9 @@ def test_step_graph_replays_match_eager(pk, name, kw):
     with eager work and synchronizations between replays."""
     import torch
 
-    announce(f"graph replay {name}")
+    announce(f"graph replay {name} {kw}")
+    kw = dict(kw)
+    split = kw.pop("split", False)
     wl = synth.make(name, **kw)
     tc, _ = tables_both(pk, wl)
     dev = runner.gpu_setup(wl, tc)
@@ -610,9 +614,11 @@ def test_step_graph_replays_match_eager(pk, name, kw):
                                          runner.decode_max_seq_len(wl), partition_tokens=wl.partition_tokens,
                                          workspace=ws, stream=s, prepare=True))
     else:
+        pws = runner.prefill_workspace(wl) if split else None
+        assert not split or pws is not None
         calls.append(pk.paged_attn_prefill_chunk(out, d["q"], d["k_pool"], d["v_pool"], d["tables"], dev["_cu_q"],
                                                  dev["_seq_lens"], int(wl.chunk_lens.max()), wl.scale,
-                                                 stream=s, prepare=True))
+                                                 workspace=pws, stream=s, prepare=True))
     with torch.cuda.stream(s):
         for c in calls:
             c()
