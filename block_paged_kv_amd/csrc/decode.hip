@@ -444,14 +444,13 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_lds_kernel(D
 
   const int hg = blockIdx.x;
   const int b = blockIdx.y;
-  const int p = blockIdx.z;
+  const int z = blockIdx.z;
   const int GT = a.gt;
   const int kvh = hg / a.head_groups;
   const int h0 = kvh * a.group + (hg - kvh * a.head_groups) * GT;
   const int n = a.seq_lens[b];
   const int lo = a.window > 0 ? max(0, n - a.window) : 0;
   const int s0 = (lo >> a.bs_log2) << a.bs_log2;
-  const int ps = s0 + p * a.part;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nw = blockDim.x >> 6;
@@ -480,6 +479,27 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_lds_kernel(D
   const bool spec_tbl = a.window == 0;
   int tbl_first = 0;
   if (spec_tbl) {
+    const int lb = ((z * a.part + wave * spw * kStageTokens) >> bs_log2) + lane;
+    tbl_first = lb < a.mb ? bt[lb] : 0;
+  }
+  // A row with fewer partitions than the grid runs its last partition (the
+  // partial one) from the grid's last partition slot, and that partition's
+  // own slot stays empty: the short partial partitions are then dispatched
+  // last and fill the final round of workgroups, where full ones would leave
+  // a tail (mixed-length batch 81.8 -> 79.3 us). Decided after the query and
+  // the speculative table window are requested, so that the wait for the
+  // row length does not hold them back.
+  __builtin_amdgcn_sched_barrier(0);
+  const int span_row = n - s0;
+  int p = z;
+  if (z == a.max_parts - 1) {
+    if (span_row > 0 && span_row <= z * a.part) p = (span_row - 1) / a.part;
+  } else if (span_row > z * a.part && span_row <= (z + 1) * a.part) {
+    p = a.max_parts;
+  }
+  const int ps = s0 + p * a.part;
+  if (spec_tbl && p != z && p < a.max_parts) {
+    // The moved partition's own first table window.
     const int lb = ((p * a.part + wave * spw * kStageTokens) >> bs_log2) + lane;
     tbl_first = lb < a.mb ? bt[lb] : 0;
   }
@@ -1397,7 +1417,8 @@ int32_t decode_impl(void* out, const void* q, const void* k_pool, const void* v_
   // Partition index slowest: a row whose span is shorter than max_seq_len
   // leaves its later partitions empty, and those workgroups (which only read
   // the row length before leaving) are then dispatched together near the end
-  // instead of holding slots between the streaming ones.
+  // instead of holding slots between the streaming ones; the bf16 and FP8
+  // kernel also runs such a row's last, partial partition from the last slot.
   const dim3 grid(static_cast<unsigned>(num_kv_heads * prm.head_groups),
                   static_cast<unsigned>(batch),
                   static_cast<unsigned>(pl.max_parts));

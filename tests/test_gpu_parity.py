@@ -365,6 +365,39 @@ def test_decode_invariances_bit_exact(pk):
     assert torch.equal(base[0], _outputs(pk, sub)["main"][0])
 
 
+def _one_row(wl, r):
+    """Row r of a workload without shared prefix blocks, alone."""
+    import copy
+
+    sub = copy.deepcopy(wl)
+    sub.batch = 1
+    sub.seq_lens = wl.seq_lens[r:r + 1].copy()
+    sub.tokens = [wl.tokens[r]]
+    for L, L0 in zip(sub.layers, wl.layers):
+        L.q, L.k, L.v, L.live_from = L0.q[r:r + 1], L0.k[r:r + 1], L0.v[r:r + 1], L0.live_from[r:r + 1]
+    return sub
+
+
+# Rows with fewer partitions than the grid run their last (partial) partition
+# from the grid's last partition slot (that partition's own slot stays
+# empty). Lengths end inside every position of a grid of eight 64-token
+# partitions, on a partition boundary, at one token and at the grid's end.
+@pytest.mark.parametrize("kw", [dict(head_dim=128, hq=8, hkv=2), dict(head_dim=256, hq=8, hkv=1),
+                                dict(head_dim=512, hq=4, hkv=2)], ids=["d128", "d256", "d512"])
+def test_decode_last_partition_moved(pk, kw):
+    import torch
+
+    ctx = [512, 448, 449, 200, 64, 65, 1, 511, 130, 320]
+    make = lambda: synth.make("tiny", batch=len(ctx), context=ctx, prefix=0, num_blocks=400,  # noqa: E731
+                              dtype="bf16", **kw)
+    run_case(pk, make(), label="decode-moved-last", partition_tokens=64)
+    # bit for bit what each row gives alone, where its grid has no empty slot
+    base = _outputs(pk, make(), partition_tokens=64)["main"]
+    for r in range(len(ctx)):
+        alone = _outputs(pk, _one_row(make(), r), partition_tokens=64)["main"]
+        assert torch.equal(base[r], alone[0]), (r, ctx[r])
+
+
 def test_decode_partition_sizes_agree(pk):
     import torch
 
