@@ -1175,6 +1175,9 @@ int32_t make_plan(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, int3
     const int iters = (part + iter_tokens_f32(head_dim) - 1) / iter_tokens_f32(head_dim);
     pl->nw = std::min(kMaxWaves, std::max(1, iters / 4));
   }
+  // Partition starts and ends stay well inside 32-bit positions.
+  if (static_cast<int64_t>(span) > (int64_t{1} << 30))
+    return fail(PAGED_ERR_INVALID_ARG, "max_seq_len (attended span %d) must be at most 2^30 tokens", span);
   pl->part = part;
   pl->max_parts = std::max(1, (span + part - 1) / part);
   pl->direct = pl->max_parts == 1;

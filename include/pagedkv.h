@@ -197,7 +197,8 @@ int32_t paged_attn_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
  *   seq_lens       : device, int32 [batch], each in [0, max_seq_len]
  *   partition_tokens: 0 = library rule, else a multiple of block_size in [16, 65536];
  *                  ceil(span / partition_tokens) (span = max_seq_len, or the window
- *                  plus block_size - 1 with a window) must be at most 65535
+ *                  plus block_size - 1 with a window) must be at most 65535,
+ *                  and the span at most 2^30 tokens (PAGED_ERR_INVALID_ARG otherwise)
  *   workspace      : device, >= paged_attn_decode_workspace_bytes(...) bytes
  * For a KV-shared layer pass the anchor layer's pools and tables; for a
  * sliding layer pass its own pool, tables and window. */

@@ -134,6 +134,15 @@ def test_partition_count_limit():
         2 * 4 * 65535 * (128 + 2) * 4
 
 
+def test_span_limit():
+    # an attended span above 2^30 tokens is rejected (positions stay in 32 bits)
+    assert pk.paged_attn_decode_workspace_bytes(1, 8, 1, 128, 16, 1 << 30, 0, 65536, "bf16") > 0
+    with pytest.raises(pk.PagedError, match="2\\^30"):
+        pk.paged_attn_decode_workspace_bytes(1, 8, 1, 128, 16, (1 << 30) + 1, 0, 65536, "bf16")
+    # a window bounds the span whatever max_seq_len is
+    assert pk.paged_attn_decode_workspace_bytes(1, 8, 1, 128, 16, 2**31 - 1, 512, 64, "bf16") > 0
+
+
 def test_mixed_step_argument_errors():
     L = pk.lib
 
