@@ -13,7 +13,8 @@
 //     workgroup has eight waves (four inside the mixed step up to head_dim
 //     128). At head_dim 512 the waves come in pairs over the same 16 rows,
 //     each holding half of head_dim.
-//   * K/V tiles of 64 keys (32 at head_dim 512) are staged in LDS, both
+//   * K/V tiles of 128 keys (bf16 up to head_dim 128, eight waves), 64
+//     (others) or 32 (head_dim 512) are staged in LDS, both
 //     row-major (key, head_dim); the P.V operand is read with a transposing
 //     LDS read (ds_read_b64_tr_b16), which hands each lane consecutive keys.
 //     Operand reads run a few fragments ahead of the products.
@@ -39,9 +40,18 @@ namespace {
 // Query rows per wave: 32 (two 16-row MFMA tiles) up to head_dim 128, 16 from
 // head_dim 256, where two tiles' accumulators would leave one wave per SIMD.
 constexpr int rows_per_wave(int d) { return d >= 256 ? 16 : 32; }
-// Keys per K/V tile: 64, except 32 at head_dim 512, where two buffers of 64
-// one-KiB key rows (K and V) would not fit in a CU's 160 KiB of LDS.
-constexpr int tile_keys(int d) { return d >= 512 ? 32 : 64; }
+// Keys per K/V tile. 128 for bf16 pools up to head_dim 128 with eight-wave
+// workgroups: the double-buffered K and V tiles take 128 KiB of LDS, and
+// half as many tiles per row halve the barriers and per-tile softmax
+// bookkeeping (the 2048-token chunk over a 63488-token prefix 1.90 ->
+// 1.82 ms). 64 otherwise: four-wave workgroups must keep two per CU beside
+// the decode of the mixed step (the doubled score and probability registers
+// would not fit), FP8 staging registers would spill, and at head_dim 256 two
+// 128-key buffers would not fit the LDS. 32 at head_dim 512, where two
+// buffers of 64 one-KiB key rows (K and V) would not fit in a CU's 160 KiB.
+constexpr int tile_keys(int d, int nw, int esz) {
+  return d >= 512 ? 32 : (d <= 128 && nw == 8 && esz == 2) ? 128 : 64;
+}
 // Waves that share a set of query rows and split the head dimension between
 // them: two at head_dim 512, one below. Each of the two holds half of the
 // query operands, computes the partial scores over its half, exchanges them
@@ -100,7 +110,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
   constexpr int RPW = rows_per_wave(D);
   constexpr int JT = RPW / 16;  // 16-row query tiles per wave
   constexpr int kTileM = RG * RPW;
-  constexpr int kTileN = tile_keys(D);
+  constexpr int kTileN = tile_keys(D, NW, ESZ);
   constexpr int NS = kTileN / 16;    // 16-key sub-tiles per tile (S^T column tiles)
   constexpr int NK = kTileN / 32;    // 32-key MFMA steps of P.V per tile
   // LDS tiles: key rows of D bf16 elements, unpadded; the 16-byte chunks of
@@ -238,7 +248,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
   // entries by readlane, so block bases are wave-uniform and each lane adds a
   // loop-invariant 32-bit offset.
   constexpr int RPI = 64 / DCH;                   // key rows per load instruction
-  constexpr int KPW = kTileN / kWaves;            // keys each wave stages (16, 8 or 4)
+  constexpr int KPW = kTileN / kWaves;            // keys each wave stages (4 to 16)
   constexpr int KI = KPW / RPI;                   // load instructions per wave per tile (K, and V)
   const bool bs8 = bs_log2 == 3;
   const bool split = bs8 && KPW > 8;              // the wave's keys span two blocks
