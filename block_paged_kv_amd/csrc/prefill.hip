@@ -46,8 +46,8 @@ constexpr int rows_per_wave(int d) { return d >= 256 ? 16 : 32; }
 // bookkeeping (the 2048-token chunk over a 63488-token prefix 1.90 ->
 // 1.82 ms). 64 otherwise: four-wave workgroups must keep two per CU beside
 // the decode of the mixed step (the doubled score and probability registers
-// would not fit), FP8 staging registers would spill, and at head_dim 256 two
-// 128-key buffers would not fit the LDS. 32 at head_dim 512, where two
+// would not fit), FP8 staging registers spill (measured 1.7x slower), and at
+// head_dim 256 two 128-key buffers would not fit the LDS. 32 at head_dim 512, where two
 // buffers of 64 one-KiB key rows (K and V) would not fit in a CU's 160 KiB.
 constexpr int tile_keys(int d, int nw, int esz) {
   return d >= 512 ? 32 : (d <= 128 && nw == 8 && esz == 2) ? 128 : 64;
