@@ -263,24 +263,40 @@ def time_serial_mixed_step(pk, wl, dev, outs, ws, stream, steps):
     import runner
 
     nd = wl.num_decode
+    fp8 = wl.kv_dtype == "fp8"
     calls = []
     for L in wl.layers:
         if L.alias_of:
             continue
         d = dev[L.name]
-        calls.append(pk.paged_kv_write(d["k_pool"], d["v_pool"], d["step_k"], d["step_v"], d["step_slots"],
-                                       stream=stream, prepare=True))
+        if fp8:
+            calls.append(pk.paged_kv_write_fp8(d["k_pool"], d["v_pool"], d["step_k"], d["step_v"], d["step_slots"],
+                                               L.k_scale, L.v_scale, stream=stream, prepare=True))
+        else:
+            calls.append(pk.paged_kv_write(d["k_pool"], d["v_pool"], d["step_k"], d["step_v"], d["step_slots"],
+                                           stream=stream, prepare=True))
     for L in wl.layers:
         d = dev[L.name]
         o = outs[L.name]
-        calls.append(pk.paged_attn_decode(o[:nd], d["q"][:nd], d["k_pool"], d["v_pool"], d["tables"][:nd],
-                                          dev["_seq_lens"][:nd], wl.scale, runner.decode_max_seq_len(wl),
-                                          sliding_window=L.window, partition_tokens=wl.partition_tokens,
-                                          workspace=ws, stream=stream, prepare=True))
-        calls.append(pk.paged_attn_prefill_chunk(o, d["q"], d["k_pool"], d["v_pool"], d["tables"][nd:],
-                                                 dev["_cu_q"][nd:], dev["_seq_lens"][nd:],
-                                                 int(wl.chunk_lens.max()), wl.scale, sliding_window=L.window,
-                                                 stream=stream, prepare=True))
+        msl = runner.decode_max_seq_len(wl)
+        chunk = int(wl.chunk_lens.max())
+        if fp8:
+            calls.append(pk.paged_attn_decode_fp8(o[:nd], d["q"][:nd], d["k_pool"], d["v_pool"], d["tables"][:nd],
+                                                  dev["_seq_lens"][:nd], wl.scale, L.k_scale, L.v_scale, msl,
+                                                  sliding_window=L.window, partition_tokens=wl.partition_tokens,
+                                                  workspace=ws, stream=stream, prepare=True))
+            calls.append(pk.paged_attn_prefill_chunk_fp8(o, d["q"], d["k_pool"], d["v_pool"], d["tables"][nd:],
+                                                         dev["_cu_q"][nd:], dev["_seq_lens"][nd:], chunk, wl.scale,
+                                                         L.k_scale, L.v_scale, sliding_window=L.window,
+                                                         stream=stream, prepare=True))
+        else:
+            calls.append(pk.paged_attn_decode(o[:nd], d["q"][:nd], d["k_pool"], d["v_pool"], d["tables"][:nd],
+                                              dev["_seq_lens"][:nd], wl.scale, msl, sliding_window=L.window,
+                                              partition_tokens=wl.partition_tokens, workspace=ws, stream=stream,
+                                              prepare=True))
+            calls.append(pk.paged_attn_prefill_chunk(o, d["q"], d["k_pool"], d["v_pool"], d["tables"][nd:],
+                                                     dev["_cu_q"][nd:], dev["_seq_lens"][nd:], chunk, wl.scale,
+                                                     sliding_window=L.window, stream=stream, prepare=True))
     with torch.cuda.stream(stream):
         for c in calls:
             c()

@@ -27,9 +27,7 @@ int32_t decode_check(const void* out, const void* q, const void* k_pool, const v
                      const void* workspace, size_t workspace_bytes, int esz);
 
 // Chunked prefill over pools of esz-byte elements (2 bf16, 1 FP8 codes); q and
-// out bf16. cu_q_lens holds absolute offsets into q and out. waves: 4 or 8
-// waves per workgroup up to head_dim 128 (head_dim 256 and 512 take 8
-// whatever is asked), 0 for the default. workspace NULL: no key split; else
+// out bf16. cu_q_lens holds absolute offsets into q and out. workspace NULL: no key split; else
 // the key split of the library rule, its partials in the workspace.
 // beside_decode: the launch shares the device with decode work (mixed step),
 // which changes only the order the query tiles are dispatched in.
@@ -40,7 +38,7 @@ int32_t prefill_impl(void* out, const void* q, const void* k_pool, const void* v
                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                      int32_t num_blocks, float scale, float k_scale, float v_scale,
                      int32_t sliding_window, void* workspace, size_t workspace_bytes, int esz,
-                     void* stream, int waves = 0, bool beside_decode = false);
+                     void* stream, bool beside_decode = false);
 
 // Every argument check of prefill_impl, with nothing enqueued.
 int32_t prefill_check(const void* out, const void* q, const void* k_pool, const void* v_pool,

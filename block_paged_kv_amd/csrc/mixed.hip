@@ -65,17 +65,14 @@ extern "C" int32_t paged_attn_mixed(void* out, const void* q, const void* k_pool
   SideStream side(s);
   if (side.status() != PAGED_OK) return side.status();
   // Chunk rows first (the long kernel starts first), on the side stream: their
-  // cu_q_lens entries are absolute offsets into q and out. Up to head_dim 128
-  // the prefill runs four-wave workgroups, two per CU: once one of them
-  // finishes, decode workgroups fit beside the other (an eight-wave workgroup
-  // would hold its CU's registers until the end). At head_dim 256 and 512 the
-  // prefill keeps its own shape (eight and four waves), whose tiles take most
-  // of a CU's LDS.
+  // cu_q_lens entries are absolute offsets into q and out. The prefill keeps
+  // its own workgroup shape; its query tiles go first-first (the default
+  // order is last-first), which suited the decode beside it.
   int32_t rc = prefill_impl(out, q, k_pool, v_pool, block_tables + static_cast<size_t>(nd) * max_blocks_per_seq,
                             max_blocks_per_seq, cu_q_lens + nd, seq_lens + nd, np, total_q - nd,
                             max_q_len, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                             scale, k_scale, v_scale, sliding_window, /*workspace=*/nullptr, 0, esz,
-                            side.get(), /*waves=*/4, /*beside_decode=*/true);
+                            side.get(), /*beside_decode=*/true);
   if (rc == PAGED_OK)
     rc = decode_impl(out, q, k_pool, v_pool, block_tables, max_blocks_per_seq, seq_lens, nd,
                      num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, k_scale,

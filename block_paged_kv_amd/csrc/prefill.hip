@@ -40,18 +40,14 @@ namespace {
 // Query rows per wave: 32 (two 16-row MFMA tiles) up to head_dim 128, 16 from
 // head_dim 256, where two tiles' accumulators would leave one wave per SIMD.
 constexpr int rows_per_wave(int d) { return d >= 256 ? 16 : 32; }
-// Keys per K/V tile. 128 for bf16 pools up to head_dim 128 with eight-wave
-// workgroups: the double-buffered K and V tiles take 128 KiB of LDS, and
-// half as many tiles per row halve the barriers and per-tile softmax
-// bookkeeping (the 2048-token chunk over a 63488-token prefix 1.90 ->
-// 1.82 ms). 64 otherwise: four-wave workgroups must keep two per CU beside
-// the decode of the mixed step (the doubled score and probability registers
-// would not fit), FP8 staging registers spill (measured 1.7x slower), and at
-// head_dim 256 two 128-key buffers would not fit the LDS. 32 at head_dim 512, where two
-// buffers of 64 one-KiB key rows (K and V) would not fit in a CU's 160 KiB.
-constexpr int tile_keys(int d, int nw, int esz) {
-  return d >= 512 ? 32 : (d <= 128 && nw == 8 && esz == 2) ? 128 : 64;
-}
+// Keys per K/V tile. 128 for bf16 pools up to head_dim 128: the
+// double-buffered K and V tiles take 128 KiB of LDS, and half as many tiles
+// per row halve the barriers and per-tile softmax bookkeeping (the
+// 2048-token chunk over a 63488-token prefix 1.90 -> 1.82 ms). 64 otherwise:
+// FP8 staging registers spill at 128 (measured 1.7x slower), and at head_dim
+// 256 two 128-key buffers would not fit the LDS. 32 at head_dim 512, where
+// two buffers of 64 one-KiB key rows (K and V) would not fit in a CU's 160 KiB.
+constexpr int tile_keys(int d, int esz) { return d >= 512 ? 32 : (d <= 128 && esz == 2) ? 128 : 64; }
 // Waves that share a set of query rows and split the head dimension between
 // them: two at head_dim 512, one below. Each of the two holds half of the
 // query operands, computes the partial scores over its half, exchanges them
@@ -60,13 +56,13 @@ constexpr int tile_keys(int d, int nw, int esz) {
 // two waves per SIMD, where one wave holding all 512 columns needed the
 // whole register file of its SIMD.
 constexpr int splits(int d) { return d >= 512 ? 2 : 1; }
-// Waves per workgroup: eight by default (up to head_dim 128, 256 query rows
-// share each staged K/V tile and the workgroup fills a CU's registers; at
-// head_dim 256, 8 x 16 rows, two waves per SIMD, the 128 KiB of tiles allow
-// one workgroup; at 512, four pairs of waves over 64 rows), and four up to
-// head_dim 128 when decode workgroups run beside the prefill (mixed step), so
-// that a CU can hold one of each.
-constexpr int default_waves(int) { return 8; }
+// Waves per workgroup: eight (up to head_dim 128, 256 query rows share each
+// staged K/V tile and the workgroup fills a CU's registers; at head_dim 256,
+// 8 x 16 rows, two waves per SIMD, the 128 KiB of tiles allow one workgroup;
+// at 512, four pairs of waves over 64 rows). Beside the decode of the mixed
+// step too: four-wave workgroups with 64-key tiles, two per CU so that decode
+// workgroups fit beside one of them, measured 2% slower there.
+constexpr int kPrefillWaves = 8;
 constexpr int kNumXcd = 8;
 
 typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
@@ -103,14 +99,14 @@ __device__ __forceinline__ floatx4_t mfma16x16x32(const uint4& a, const uint4& b
 // ESZ: bytes per pool element (2: bf16; 1: FP8 E4M3 codes, widened to bf16
 // exactly as they are staged, so everything after staging is shared).
 template <int D, int ESZ, int NW>
-__global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill_kernel(PrefillParams a) {
+__global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(PrefillParams a) {
   constexpr int kWaves = NW;
   constexpr int SPL = splits(D);    // waves per set of query rows
   constexpr int RG = NW / SPL;      // row groups of the workgroup
   constexpr int RPW = rows_per_wave(D);
   constexpr int JT = RPW / 16;  // 16-row query tiles per wave
   constexpr int kTileM = RG * RPW;
-  constexpr int kTileN = tile_keys(D, NW, ESZ);
+  constexpr int kTileN = tile_keys(D, ESZ);
   constexpr int NS = kTileN / 16;    // 16-key sub-tiles per tile (S^T column tiles)
   constexpr int NK = kTileN / 32;    // 32-key MFMA steps of P.V per tile
   // LDS tiles: key rows of D bf16 elements, unpadded; the 16-byte chunks of
@@ -145,8 +141,8 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D < 256) ? 2 : 1) void prefill
   // same keys of one KV head. With last_first, a row's tiles run last-first:
   // later query positions attend more keys, so the longest tiles start first
   // and the shortest fill the last round (hybrid prefill 341 -> 328 us per
-  // layer). Beside the decode of the mixed step the order stays first-first:
-  // long tiles up front there delayed the decode more than they gained.
+  // layer). Beside the decode of the mixed step the order stays first-first
+  // (last-first there: no faster with bf16 pools, 0.3% slower over FP8).
   const int tile = a.last_first ? a.tiles_per_head - 1 - item % a.tiles_per_head : item % a.tiles_per_head;
   const int rest = item / a.tiles_per_head;
   const int ksp = rest % a.ksplit;
@@ -721,8 +717,7 @@ int32_t prefill_check(const void* out, const void* q, const void* k_pool, const 
     return fail(PAGED_ERR_INVALID_ARG, "NULL pointer");
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
     return fail(PAGED_ERR_INVALID_ARG, "misaligned pointer");
-  // The largest workgroup row count (eight waves of 32 rows) gives the fewest
-  // items; four-wave launches have at most twice as many.
+  // Work items at most: 64 query rows per workgroup (the fewest, at head_dim 512).
   const int64_t items = (static_cast<int64_t>(max_q_len) * (num_q_heads / num_kv_heads) + 63) / 64 *
                         num_kv_heads * batch;
   if (items > (1LL << 30)) return fail(PAGED_ERR_INVALID_ARG, "problem too large");
@@ -731,10 +726,9 @@ int32_t prefill_check(const void* out, const void* q, const void* k_pool, const 
 
 // Query tiles (workgroups without a key split) of a launch.
 int64_t prefill_tiles(int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                      int waves, int64_t* per_head) {
+                      int64_t* per_head) {
   const int group = num_q_heads / num_kv_heads;
-  const int nw = (waves == 4 || waves == 8) && head_dim < 256 ? waves : default_waves(head_dim);
-  const int tm = nw / splits(head_dim) * rows_per_wave(head_dim);
+  const int tm = kPrefillWaves / splits(head_dim) * rows_per_wave(head_dim);
   *per_head = (static_cast<int64_t>(max_q_len) * group + tm - 1) / tm;
   return *per_head * num_kv_heads;
 }
@@ -759,7 +753,7 @@ int32_t prefill_impl(void* out, const void* q, const void* k_pool, const void* v
                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                      int32_t num_blocks, float scale, float k_scale, float v_scale,
                      int32_t sliding_window, void* workspace, size_t workspace_bytes, int esz,
-                     void* stream, int waves, bool beside_decode) {
+                     void* stream, bool beside_decode) {
   if (int32_t rc = prefill_check(out, q, k_pool, v_pool, block_tables, max_blocks_per_seq,
                                  cu_q_lens, seq_lens, batch, total_q, max_q_len, num_q_heads,
                                  num_kv_heads, head_dim, block_size, num_blocks, scale, k_scale,
@@ -768,9 +762,8 @@ int32_t prefill_impl(void* out, const void* q, const void* k_pool, const void* v
   if (workspace && !aligned16(workspace)) return fail(PAGED_ERR_INVALID_ARG, "misaligned workspace");
   if (batch == 0 || total_q == 0 || max_q_len == 0) return ok();
   const int group = num_q_heads / num_kv_heads;
-  const int nw = (waves == 4 || waves == 8) && head_dim < 256 ? waves : default_waves(head_dim);
   int64_t tiles = 0;
-  const int64_t items1 = prefill_tiles(max_q_len, num_q_heads, num_kv_heads, head_dim, waves, &tiles) * batch;
+  const int64_t items1 = prefill_tiles(max_q_len, num_q_heads, num_kv_heads, head_dim, &tiles) * batch;
   int ksplit = 1;
   if (workspace) {
     const int cus = device_cu_count();
@@ -812,23 +805,23 @@ int32_t prefill_impl(void* out, const void* q, const void* k_pool, const void* v
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid(static_cast<unsigned>(prm.per_xcd * kNumXcd));
-  const dim3 block(nw * 64);
+  const dim3 block(kPrefillWaves * 64);
   LaunchTrace tr(PAGED_KERNEL_PREFILL, s);
   auto launch = [&](auto kern) {
     hipExtLaunchKernelGGL(kern, grid, block, 0, s, tr.start(), tr.stop(), 0, prm);
   };
   if (head_dim == 512) {
-    if (esz == 1) launch(prefill_kernel<512, 1, 8>);
-    else launch(prefill_kernel<512, 2, 8>);
+    if (esz == 1) launch(prefill_kernel<512, 1, kPrefillWaves>);
+    else launch(prefill_kernel<512, 2, kPrefillWaves>);
   } else if (head_dim == 256) {
-    if (esz == 1) launch(prefill_kernel<256, 1, 8>);
-    else launch(prefill_kernel<256, 2, 8>);
+    if (esz == 1) launch(prefill_kernel<256, 1, kPrefillWaves>);
+    else launch(prefill_kernel<256, 2, kPrefillWaves>);
   } else if (head_dim == 128) {
-    if (esz == 1) nw == 8 ? launch(prefill_kernel<128, 1, 8>) : launch(prefill_kernel<128, 1, 4>);
-    else nw == 8 ? launch(prefill_kernel<128, 2, 8>) : launch(prefill_kernel<128, 2, 4>);
+    if (esz == 1) launch(prefill_kernel<128, 1, kPrefillWaves>);
+    else launch(prefill_kernel<128, 2, kPrefillWaves>);
   } else {
-    if (esz == 1) nw == 8 ? launch(prefill_kernel<64, 1, 8>) : launch(prefill_kernel<64, 1, 4>);
-    else nw == 8 ? launch(prefill_kernel<64, 2, 8>) : launch(prefill_kernel<64, 2, 4>);
+    if (esz == 1) launch(prefill_kernel<64, 1, kPrefillWaves>);
+    else launch(prefill_kernel<64, 2, kPrefillWaves>);
   }
   tr.finish();
   if (ksplit > 1) {
@@ -898,7 +891,7 @@ extern "C" int32_t paged_attn_prefill_chunk_workspace_bytes(int32_t batch, int32
   const int cus = device_cu_count();
   if (cus <= 0) return fail(PAGED_ERR_HIP, "cannot query the device compute-unit count");
   int64_t tiles = 0;
-  const int64_t items = prefill_tiles(max_q_len, num_q_heads, num_kv_heads, head_dim, 0, &tiles) * batch;
+  const int64_t items = prefill_tiles(max_q_len, num_q_heads, num_kv_heads, head_dim, &tiles) * batch;
   *bytes = prefill_ws_bytes(prefill_key_splits(items, cus), total_q, num_q_heads, head_dim);
   return ok();
 }
