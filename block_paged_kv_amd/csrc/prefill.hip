@@ -10,11 +10,10 @@
 //   * Query rows are (position, query head) pairs of one KV head, packed
 //     position-major, so the G query heads sharing a KV head share every K/V
 //     tile. A wave owns 32 rows up to head_dim 128 and 16 beyond; a
-//     workgroup has eight waves (four inside the mixed step up to head_dim
-//     128). At head_dim 512 the waves come in pairs over the same 16 rows,
-//     each holding half of head_dim.
-//   * K/V tiles of 128 keys (bf16 up to head_dim 128, eight waves), 64
-//     (others) or 32 (head_dim 512) are staged in LDS, both
+//     workgroup has eight waves. At head_dim 512 the waves come in pairs
+//     over the same 16 rows, each holding half of head_dim.
+//   * K/V tiles of 128 keys (bf16 up to head_dim 128), 64 (others) or 32
+//     (head_dim 512) are staged in LDS, both
 //     row-major (key, head_dim); the P.V operand is read with a transposing
 //     LDS read (ds_read_b64_tr_b16), which hands each lane consecutive keys.
 //     Operand reads run a few fragments ahead of the products.
