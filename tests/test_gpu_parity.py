@@ -686,18 +686,18 @@ def test_step_graph_replays_match_eager(pk, name, kw):
 
 # --------------------------------------------------------------- absent table entries
 @pytest.mark.parametrize("kind", ["decode", "prefill", "mixed"])
-@pytest.mark.parametrize("d", [128, 256])
-def test_absent_entries_get_no_weight(pk, kind, d):
+@pytest.mark.parametrize("d,bs", [(128, 16), (256, 16), (128, 8)])
+def test_absent_entries_get_no_weight(pk, kind, d, bs):
     """Table entries that are 0, past num_blocks, or columns past the table's
     width, inside the attended range: decode, prefill and the mixed step all
     treat those keys as absent (weight zero). Expected: the oracle's plain
     attention over the keys that remain."""
     import torch
 
-    announce(f"absent entries {kind} D={d}")
+    announce(f"absent entries {kind} D={d} block_size={bs}")
     rng = np.random.default_rng(31)
-    bs, hq, hkv, nb, mb = 16, 4, 2, 40, 6
-    lens = [100, 75]                        # row 0 needs 7 blocks: column 6 lies past the width
+    hq, hkv, nb, mb = 4, 2, 40, 6
+    lens = [100, 75]                        # rows longer than 6 blocks: later columns lie past the width
     chunks = {"decode": [1, 1], "prefill": [20, 10], "mixed": [1, 10]}[kind]
     perm = list(rng.permutation(np.arange(1, nb)))
     tables = np.zeros((2, mb), dtype=np.int32)
@@ -715,7 +715,8 @@ def test_absent_entries_get_no_weight(pk, kind, d):
             vp[tables[b, j], :, :min(bs, n - j * bs)] = fv[j * bs:(j + 1) * bs].transpose(1, 0, 2)
     tables[0, 2] = 0            # a null entry inside row 0's range
     tables[1, 1] = nb + 5       # an out-of-range block id inside row 1's range
-    absent = [set(range(32, 48)) | set(range(96, 100)), set(range(16, 32))]
+    absent = [set(range(2 * bs, 3 * bs)) | set(range(mb * bs, lens[0])),
+              set(range(bs, 2 * bs)) | set(range(mb * bs, lens[1]))]
     kp = np.nan_to_num(kp, nan=0.0)      # never-written slots of used blocks hold zeros
     vp = np.nan_to_num(vp, nan=0.0)
     kp[0] = np.nan                       # the null block: must never be read
